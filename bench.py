@@ -1,0 +1,226 @@
+"""Throughput of the DBO expert-parallel MoE layer on one MI355X.
+
+One step = one dbo_moe_layer call over one batch of synthetic input (routing,
+dispatch, grouped SwiGLU FFN and combine of both microbatches, both streams
+joined).  Default workload: the DeepSeek-V2-Lite-shaped decode layer (T=256
+tokens split 128/128, H=2048, 64 routed experts top-6 + 2 shared experts,
+I=1408, bf16).  Prints one JSON line with the DBO tokens/s, the SERIAL
+tokens/s beside it, the roofline of the dominant kernel (the gate/up expert
+GEMM), and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+KERNEL_SOURCES = ["combine_dual_overlap_amd/csrc/gemm_mfma.h", "combine_dual_overlap_amd/csrc/ffn.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per gate/up launch from the committed rocprofv3 --pmc summary,
+    or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"ffn_gate_up_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def gateup_work(cfg, counts_per_mb):
+    """Algorithmic bytes and flops of one gate/up GEMM launch per microbatch:
+    weights of every expert that received rows (read once), the dispatched
+    rows (read once), the SwiGLU output h (written once)."""
+    w_s = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
+    a_s = 4 if cfg.act == "f32" else 2
+    out = []
+    for counts in counts_per_mb:
+        hit = int((counts > 0).sum())
+        M = int(counts.sum())
+        wbytes = hit * 2 * cfg.I * cfg.H * w_s
+        if cfg.wdt == "fp8":
+            wbytes += hit * (2 * cfg.I // 128) * (cfg.H // 128) * 4
+        nbytes = wbytes + M * cfg.H * a_s + M * cfg.I * a_s
+        flops = 2.0 * M * cfg.H * 2 * cfg.I
+        out.append((nbytes, flops))
+    return out
+
+
+def cpu_baseline(inp, cfg, budget_s: float):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    its first tokens (all of them when one run fits the budget)."""
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    ov = W.oracle_view(inp)
+    n = cfg.T if cfg.T <= 512 else 512
+    sub = O.slice_view(ov, 0, n)
+    t0 = time.perf_counter()
+    O.moe_layer_expert(sub)
+    dt = time.perf_counter() - t0
+    if dt > budget_s and n > 8:
+        n = max(8, int(n * budget_s / dt))
+        sub = O.slice_view(ov, 0, n)
+        t0 = time.perf_counter()
+        O.moe_layer_expert(sub)
+        dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} tokens of the workload, float64 numpy/BLAS moe_layer_expert, one run {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="layer configuration 1..5 (default 2)")
+    ap.add_argument("--schedule", default="dbo", choices=["dbo", "serial", "unsplit", "dbo_late_event"])
+    ap.add_argument("--comm-cu-budget", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the layer is one GPU's share of the expert-parallel work "
+              f"and no multi-GPU path is built (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    from combine_dual_overlap_amd import DeviceLayer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = W.get_config(args.config)
+    log(f"bench: generating {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I}")
+    inp = W.make_inputs(cfg)
+    L = DeviceLayer(inp, device="cuda:0")
+    K, Wm = args.steps, args.warmup
+    T = cfg.T
+
+    def run(sched):
+        L.run(sched, comm_cu_budget=args.comm_cu_budget)
+
+    def timed(sched):
+        for _ in range(Wm):
+            run(sched)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            run(sched)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    log(f"bench: warmup {Wm}, timing {K} steps of {args.schedule} and serial")
+    dt = timed(args.schedule)
+    dt_serial = timed("serial")
+    dt_unsplit = timed("unsplit")
+
+    # Kernel timing: events around each microbatch's gate/up and down GEMMs on
+    # the compute stream, over K more steps of the same schedule.
+    L.ctx.set_timing(True)
+    for _ in range(min(K, 128)):
+        run(args.schedule)
+    torch.cuda.synchronize()
+    n_t = min(K, 128)
+    times = np.array([L.ctx.ffn_times(b) for b in range(n_t)])     # [n, 4] ms
+    L.ctx.set_timing(False)
+    gu_ms = times[:, [0, 2]]
+    gu_ms = gu_ms[gu_ms > 0]
+    dn_ms = times[:, [1, 3]]
+    dn_ms = dn_ms[dn_ms > 0]
+
+    T0 = L.ctx.last_stats()["T0"]
+    halves = [(0, T0), (T0, T)] if T0 < T else [(0, T)]
+    counts = [L.view(mb, "counts", torch.int32, (cfg.E_loc,), T=T).cpu().numpy() for mb in range(len(halves))]
+    work = gateup_work(cfg, counts)
+    bytes_launch = float(np.mean([w[0] for w in work]))
+    flops_launch = float(np.mean([w[1] for w in work]))
+    avg_s = float(np.mean(gu_ms)) / 1e3
+    ai = flops_launch / bytes_launch
+    mfma_peak = MFMA_PEAK_TFLOPS["f32" if cfg.act == "f32" else "bf16"]
+    hbm_bound = ai < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = read_traffic(f"c{args.config}")
+    if hbm_bound:
+        achieved = bytes_launch / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = flops_launch / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(achieved / mfma_peak, 4)}
+    roof["traffic"] = traffic
+    roof["kernel"] = "gate/up expert GEMM + SwiGLU (k_gemm_nt MODE_GATEUP)"
+    roof["avg_launch_us"] = round(avg_s * 1e6, 2)
+    roof["algorithmic_bytes_per_launch"] = int(bytes_launch)
+    roof["algorithmic_flops_per_launch"] = int(flops_launch)
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        base = cpu_baseline(inp, cfg, args.cpu_budget_s)
+
+    value = T * K / dt
+    dtype = {"f32": "f32", "bf16": "bf16"}[cfg.act]
+    rec = {
+        "metric": "MoE-layer tokens/sec (DBO vs serial) + MFMA util % and HBM GB/s % of peak",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(dt / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded random activations and weights of the layer's shape)",
+        "config": {"workload": cfg.name, "T": T, "split": [T0, T - T0] if T0 < T else [T], "H": cfg.H,
+                   "E": cfg.E, "E_local": cfg.E_loc, "k": cfg.k, "I": cfg.I, "shared_experts": cfg.n_shared,
+                   "weights": cfg.wdt, "schedule": args.schedule, "comm_cu_budget": args.comm_cu_budget},
+        "serial_tokens_per_s": round(T * K / dt_serial, 1),
+        "unsplit_tokens_per_s": round(T * K / dt_unsplit, 1),
+        "dbo_speedup_vs_serial": round(dt_serial / dt, 4),
+        "kernel_ms": {"gate_up_avg": round(float(np.mean(gu_ms)), 4), "down_avg": round(float(np.mean(dn_ms)), 4)},
+        "roofline": roof,
+        "cpu_baseline": base,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

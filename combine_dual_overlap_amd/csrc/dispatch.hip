@@ -1,0 +1,275 @@
+// Dispatch: stable counting sort of (token, slot) pairs by local expert and the
+// row gather into contiguous per-expert rows, for gfx950.
+//
+// Single-GPU stand-in for the all-to-all dispatch of "[Core/DBO][1/N] Add
+// Dual-Batch Overlap mechanism to VLLM", Purpose.  Per-expert counts are produced
+// and kept on the device and every buffer is sized for the worst case of T*k
+// rows ("DeepEP HT: full decode CUDA graphs via worst-token dispatch", bot
+// review 2), so nothing waits on the host.
+//
+// Four kernels, each a pass over HBM-resident data:
+//  1. count   - one workgroup per 256 pairs: LDS histogram of local experts;
+//               flags ids outside [0, E).
+//  2. scan    - one workgroup: per expert, exclusive prefix over the blocks
+//               (stable block bases), then counts -> offsets (and tile offsets).
+//  3. rank    - one workgroup per 256 pairs: stable rank of every pair inside its
+//               block from wave ballots (lanes holding the same expert are
+//               grouped with a ballot loop; rank = popcount of lower lanes) plus
+//               an LDS prefix over the 4 waves; writes perm and inv.
+//  4. gather  - one wave per token: the row is read from HBM once (16-byte
+//               vector loads, several in flight per lane) and written to each of
+//               its k destination rows.
+#include "common.h"
+
+namespace dbomoe {
+
+constexpr int kPairsPerBlock = 256;
+constexpr int kMaxELoc = 1024;
+
+static inline int64_t n_pair_blocks(int64_t T, int32_t k) {
+  return (T * k + kPairsPerBlock - 1) / kPairsPerBlock;
+}
+
+size_t dispatch_ws_bytes(int64_t T, int32_t k, int32_t E_loc) {
+  const int64_t nb = n_pair_blocks(T, k);
+  return align_up(static_cast<size_t>(nb) * E_loc * 4, 256) + align_up(static_cast<size_t>(nb) * 4, 256) + 256;
+}
+
+struct DispWs {
+  int32_t* block_hist;  // [nb][E_loc]; after the scan: stable base of the block inside each expert
+  int32_t* block_err;   // [nb]
+  int32_t* err;         // [1]
+};
+
+// Layout: error word at offset 0 (so it can be found without the shapes),
+// then the per-block error flags, then the per-block histograms.
+static DispWs carve(void* ws, int64_t nb, int32_t E_loc) {
+  (void)E_loc;
+  char* b = static_cast<char*>(ws);
+  DispWs d;
+  d.err = reinterpret_cast<int32_t*>(b);
+  b += 256;
+  d.block_err = reinterpret_cast<int32_t*>(b);
+  b += align_up(static_cast<size_t>(nb) * 4, 256);
+  d.block_hist = reinterpret_cast<int32_t*>(b);
+  return d;
+}
+
+__global__ __launch_bounds__(256) void k_disp_count(const int32_t* __restrict__ ids, int64_t n_pairs,
+                                                    int E_total, int e_begin, int E_loc,
+                                                    int32_t* __restrict__ block_hist,
+                                                    int32_t* __restrict__ block_err) {
+  __shared__ int hist[kMaxELoc];
+  for (int e = threadIdx.x; e < E_loc; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * kPairsPerBlock + threadIdx.x;
+  int bad = 0;
+  if (p < n_pairs) {
+    const int e = ids[p];
+    if (e < 0 || e >= E_total) {
+      bad = 1;
+    } else {
+      const int le = e - e_begin;
+      if (le >= 0 && le < E_loc) atomicAdd(&hist[le], 1);
+    }
+  }
+  bad = __syncthreads_or(bad);
+  int32_t* out = block_hist + static_cast<int64_t>(blockIdx.x) * E_loc;
+  for (int e = threadIdx.x; e < E_loc; e += 256) out[e] = hist[e];
+  if (threadIdx.x == 0) block_err[blockIdx.x] = bad;
+}
+
+// Exclusive scan of v over the first n <= 1024 threads of a 1024-thread block.
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < 16 ? s_wsum[lane] : 0;
+    const int wi = wave_incl_scan(w);
+    if (lane < 16) s_wsum[16 + lane] = wi - w;
+  }
+  __syncthreads();
+  const int r = s_wsum[16 + wave] + incl - v;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void k_disp_scan(int64_t nb, int E_loc, int tile_m,
+                                                    int32_t* __restrict__ block_hist,
+                                                    const int32_t* __restrict__ block_err,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ tile_offsets,
+                                                    int32_t* __restrict__ err) {
+  __shared__ int s_wsum[32];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E_loc) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const int64_t i = b * E_loc + e;
+      const int v = block_hist[i];
+      block_hist[i] = cnt;
+      cnt += v;
+    }
+    counts[e] = cnt;
+  }
+  const int off = block_excl_scan_1024(cnt, s_wsum);
+  if (e < E_loc) offsets[e] = off;
+  if (e == E_loc - 1) offsets[E_loc] = off + cnt;
+  if (tile_offsets) {
+    const int tiles = (cnt + tile_m - 1) / tile_m;
+    const int toff = block_excl_scan_1024(tiles, s_wsum);
+    if (e < E_loc) tile_offsets[e] = toff;
+    if (e == E_loc - 1) tile_offsets[E_loc] = toff + tiles;
+  }
+  if (threadIdx.x == 0) {
+    int any = 0;
+    for (int64_t b = 0; b < nb; ++b) any |= block_err[b];
+    err[0] = any;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_disp_rank(const int32_t* __restrict__ ids, int64_t n_pairs,
+                                                   int e_begin, int E_loc,
+                                                   const int32_t* __restrict__ block_base,
+                                                   const int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int wave_cnt[4][kMaxELoc];
+  for (int i = threadIdx.x; i < 4 * E_loc; i += 256) wave_cnt[i / E_loc][i % E_loc] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * kPairsPerBlock + threadIdx.x;
+  int le = -1;
+  if (p < n_pairs) {
+    const int e = ids[p] - e_begin;
+    if (e >= 0 && e < E_loc) le = e;
+  }
+  const bool local = le >= 0;
+  // Group the lanes of this wave by expert: one ballot per distinct expert.
+  uint64_t remaining = __ballot(local);
+  uint64_t mine = 0;
+  while (remaining) {
+    const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+    const int lead_e = __shfl(le, leader, kWave);
+    const uint64_t m = __ballot(local && le == lead_e);
+    if (local && le == lead_e) mine = m;
+    remaining &= ~m;
+  }
+  const uint64_t lower = mine & lanemask_lt();
+  if (local && lower == 0) wave_cnt[wave][le] = __popcll(mine);
+  __syncthreads();
+  if (p < n_pairs) {
+    int pos = -1;
+    if (local) {
+      pos = offsets[le] + block_base[static_cast<int64_t>(blockIdx.x) * E_loc + le] + __popcll(lower);
+      for (int w = 0; w < wave; ++w) pos += wave_cnt[w][le];
+      perm[pos] = static_cast<int32_t>(p);
+    }
+    inv[p] = pos;
+  }
+}
+
+// One wave per token; rows are moved as 16-byte chunks, kChunks per lane in
+// flight at a time.
+constexpr int kChunks = 4;
+
+__global__ __launch_bounds__(256) void k_disp_gather(const u32x4_t* __restrict__ x, int64_t T, int row_chunks,
+                                                     int k, const int32_t* __restrict__ inv,
+                                                     u32x4_t* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave; t < T; t += stride) {
+    const u32x4_t* src = x + t * row_chunks;
+    for (int c0 = 0; c0 < row_chunks; c0 += 64 * kChunks) {
+      u32x4_t v[kChunks];
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        const int c = c0 + i * 64 + lane;
+        if (c < row_chunks) v[i] = src[c];
+      }
+      for (int j = 0; j < k; ++j) {
+        const int pos = inv[t * k + j];
+        if (pos < 0) continue;
+        u32x4_t* dst = x_perm + static_cast<int64_t>(pos) * row_chunks;
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+          const int c = c0 + i * 64 + lane;
+          if (c < row_chunks) dst[c] = v[i];
+        }
+      }
+    }
+  }
+}
+
+moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  const int E_loc = a.e_end - a.e_begin;
+  const int64_t n_pairs = a.T * a.k;
+  const int64_t nb = n_pair_blocks(a.T, a.k);
+  DispWs w = carve(a.ws, nb, E_loc);
+  if (nb > 0) {
+    hipLaunchKernelGGL(k_disp_count, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a.ids, n_pairs,
+                       a.E_total, a.e_begin, E_loc, w.block_hist, w.block_err);
+    DBOMOE_CHECK_LAUNCH();
+  }
+  hipLaunchKernelGGL(k_disp_scan, dim3(1), dim3(1024), 0, s, nb, E_loc, a.tile_m > 0 ? a.tile_m : 1,
+                     w.block_hist, w.block_err, a.counts, a.offsets,
+                     a.tile_m > 0 ? a.tile_offsets : nullptr, w.err);
+  DBOMOE_CHECK_LAUNCH();
+  if (nb == 0) return MOE_OK;
+  hipLaunchKernelGGL(k_disp_rank, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a.ids, n_pairs, a.e_begin,
+                     E_loc, w.block_hist, a.offsets, a.perm, a.inv);
+  DBOMOE_CHECK_LAUNCH();
+  const int row_chunks = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
+  int64_t blocks = (a.T + 3) / 4;
+  if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
+  hipLaunchKernelGGL(k_disp_gather, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const u32x4_t*>(a.x), a.T, row_chunks, a.k, a.inv,
+                     static_cast<u32x4_t*>(a.x_perm));
+  DBOMOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+}  // namespace dbomoe
+
+using namespace dbomoe;
+
+extern "C" size_t moe_dispatch_workspace_size(int64_t T, int32_t k, int32_t E_loc) {
+  if (T < 0 || k <= 0 || E_loc <= 0) return 0;
+  return dispatch_ws_bytes(T, k, E_loc);
+}
+
+extern "C" moe_status moe_dispatch(const void* x, moe_dtype act, int64_t T, int32_t H,
+                                   const int32_t* topk_ids, int32_t k, int32_t E_total,
+                                   int32_t expert_begin, int32_t expert_end, int32_t tile_m,
+                                   int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
+                                   int32_t* perm, int32_t* inv, void* x_perm,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || H <= 0 || k < 1 || k > 16 || E_total < 1) return MOE_ERR_INVALID_ARG;
+  if (expert_begin < 0 || expert_end <= expert_begin || expert_end > E_total) return MOE_ERR_INVALID_ARG;
+  const int E_loc = expert_end - expert_begin;
+  if (E_loc > kMaxELoc) return MOE_ERR_UNSUPPORTED;
+  if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (tile_offsets && tile_m <= 0) return MOE_ERR_INVALID_ARG;
+  if (!counts || !offsets || !ws) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !topk_ids || !perm || !inv || !x_perm)) return MOE_ERR_INVALID_ARG;
+  if ((static_cast<int64_t>(H) * dtype_size(act)) % 16) return MOE_ERR_MISALIGNED;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(counts) || !aligned16(offsets) ||
+      (tile_offsets && !aligned16(tile_offsets)) || !aligned16(perm) || !aligned16(inv) ||
+      !aligned16(x_perm) || !aligned256(ws))
+    return MOE_ERR_MISALIGNED;
+  if (T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < dispatch_ws_bytes(T, k, E_loc)) return MOE_ERR_WORKSPACE;
+  DispatchArgs a{x, act, T, H, topk_ids, k, E_total, expert_begin, expert_end, tile_m,
+                 counts, offsets, tile_offsets, perm, inv, x_perm, ws, 0};
+  return launch_dispatch(a, as_stream(stream));
+}
+
+extern "C" moe_status moe_get_device_error(const void* dispatch_ws, int32_t* code, void* stream) {
+  if (!dispatch_ws || !code) return MOE_ERR_INVALID_ARG;
+  if (!aligned256(dispatch_ws)) return MOE_ERR_MISALIGNED;
+  if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return MOE_ERR_HIP;
+  if (hipMemcpy(code, dispatch_ws, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}

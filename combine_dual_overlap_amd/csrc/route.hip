@@ -1,0 +1,264 @@
+// Router logits + top-k routing (one wave per token) for gfx950.
+//
+// The pages describe the router only as the compute that precedes dispatch in
+// each microbatch ("[Core/DBO][1/N] Add Dual-Batch Overlap mechanism to VLLM",
+// Purpose); the routing rule is the stated reading in dbomoe.h.
+//
+// Logits: x [T, H] . W_r [E, H]^T on bf16 MFMA (fp32 SIMT for fp32 inputs) with
+// split-K into S fp32 partial slabs so that a 2k-token, H = 7168 microbatch still
+// fills the chip; the top-k kernel adds the S partials in a fixed order (so the
+// logits are deterministic), adds the bias and writes the logits it compares.
+// Selection compares logits, never rounded probabilities: softmax and sigmoid are
+// monotone, so the order of experts is the order of their logits.
+#include "gemm_mfma.h"
+
+namespace dbomoe {
+
+int route_splits(int64_t T, int32_t H, int32_t E) {
+  const int64_t base = (T + 31) / 32 * ((E + kBN - 1) / kBN);
+  int S = 1;
+  while (base * S < 256 && H / (S * 2) >= 256 && H % (S * 2 * kBK) == 0) S *= 2;
+  return S;
+}
+
+size_t route_ws_bytes(int64_t T, int32_t H, int32_t E) {
+  return align_up(static_cast<size_t>(route_splits(T, H, E)) * T * E * sizeof(float), 256);
+}
+
+moe_status check_route_params(const moe_route_params* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->E < 1 || p->E > 256 || p->k < 1 || p->k > 16 || p->k > p->E) return MOE_ERR_INVALID_ARG;
+  if (p->score != MOE_SCORE_SOFTMAX && p->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (p->n_groups < 1 || p->n_groups > 64 || p->E % p->n_groups) return MOE_ERR_INVALID_ARG;
+  if (p->n_groups > 1) {
+    const int per = p->E / p->n_groups;
+    if (p->topk_groups < 1 || p->topk_groups > p->n_groups) return MOE_ERR_INVALID_ARG;
+    if (p->group_topn < 1 || p->group_topn > 4 || p->group_topn > per) return MOE_ERR_INVALID_ARG;
+    if (p->k > p->topk_groups * per) return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+struct TopkParams {
+  const float* part; int S; int64_t T; int E;
+  const float* bias; const int32_t* forced; moe_route_params rp;
+  float* logits; int32_t* ids; float* w;
+};
+
+// (value desc, index asc) "better than" for the wave arg-max.
+__device__ __forceinline__ bool better(float v, int e, float ov, int oe) {
+  return v > ov || (v == ov && e < oe);
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& e) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) {
+    const float ov = __shfl_xor(v, d, kWave);
+    const int oe = __shfl_xor(e, d, kWave);
+    if (better(ov, oe, v, e)) { v = ov; e = oe; }
+  }
+}
+
+constexpr int kMaxK = 16;
+
+// One wave per token, 4 tokens per workgroup.  Lane l holds experts l, l+64, ...
+__global__ __launch_bounds__(256) void k_topk(TopkParams p) {
+  __shared__ float s_score[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (t >= p.T) return;
+  const int E = p.E;
+  const int k = p.rp.k;
+  const float NEG = -INFINITY;
+
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = NEG;
+    if (e < E) {
+      float s = 0.f;
+      for (int sp = 0; sp < p.S; ++sp) s += p.part[(sp * p.T + t) * E + e];
+      if (p.bias) s += p.bias[e];
+      v[i] = s;
+      if (p.logits) p.logits[t * E + e] = s;
+    }
+  }
+
+  const bool softmax = p.rp.score == MOE_SCORE_SOFTMAX;
+  float lmax = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  lmax = wave_max_f(lmax);
+  float denom = 0.f;
+  if (softmax) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) denom += expf(v[i] - lmax);
+    denom = wave_sum_f(denom);
+  }
+
+  // Candidate mask: bit i of lane l <=> expert l + 64 i may be selected.
+  unsigned cand = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (lane + 64 * i < E) cand |= 1u << i;
+
+  if (!softmax && p.rp.n_groups > 1 && !p.forced) {
+    // Group-limited selection: score each group by the sum of its group_topn
+    // best sigmoid scores, keep the topk_groups best groups.
+    const int G = p.rp.n_groups, per = E / G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) s_score[wave][lane + 64 * i] = 1.0f / (1.0f + expf(-v[i]));
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float gs = NEG;
+    if (lane < G) {
+      float top[4] = {NEG, NEG, NEG, NEG};
+      const int n = p.rp.group_topn;
+      for (int j = 0; j < per; ++j) {
+        float x = s_score[wave][lane * per + j];
+        // insert into the descending list top[0..n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q < n && x > top[q]) { const float tmp = top[q]; top[q] = x; x = tmp; }
+        }
+      }
+      gs = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q < n) gs += top[q];
+    }
+    uint64_t kept = 0;
+    float gv = gs;
+    for (int r = 0; r < p.rp.topk_groups; ++r) {
+      float bv = (lane < G && !((kept >> lane) & 1ull)) ? gv : NEG;
+      int be = (lane < G && !((kept >> lane) & 1ull)) ? lane : 1 << 30;
+      wave_argmax(bv, be);
+      kept |= 1ull << be;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((kept >> (e / per)) & 1ull)) cand &= ~(1u << i);
+    }
+  }
+
+  int sel_e[kMaxK];
+  float sel_v[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      int be;
+      float bv;
+      if (p.forced) {
+        be = p.forced[t * k + j];
+        bv = NEG;
+        if (be >= 0 && be < E) {
+          const int i = be >> 6, src = be & 63;
+          const float mine = i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+          bv = __shfl(mine, src, kWave);
+        }
+      } else {
+        bv = NEG;
+        be = 1 << 30;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = lane + 64 * i;
+          if (((cand >> i) & 1u) && better(v[i], e, bv, be)) { bv = v[i]; be = e; }
+        }
+        wave_argmax(bv, be);
+        if ((be & 63) == lane) cand &= ~(1u << (be >> 6));
+      }
+      sel_e[j] = be;
+      sel_v[j] = bv;
+    }
+  }
+
+  float wsum = 0.f;
+  float wj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      const bool ok = sel_e[j] >= 0 && sel_e[j] < E;
+      float w = 0.f;
+      if (ok) w = softmax ? expf(sel_v[j] - lmax) / denom : 1.0f / (1.0f + expf(-sel_v[j]));
+      wj[j] = w;
+      wsum += w;
+    }
+  }
+  const bool renorm = p.rp.renormalize != 0 && wsum > 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k && lane == j) {
+      float w = renorm ? wj[j] / wsum : wj[j];
+      p.ids[t * k + j] = sel_e[j];
+      p.w[t * k + j] = w * p.rp.routed_scale;
+    }
+  }
+}
+
+moe_status launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.T == 0) return MOE_OK;
+  const int E = a.p.E;
+  const int S = route_splits(a.T, a.H, E);
+  GemmParams g{};
+  g.A = static_cast<const bf16_t*>(a.x);
+  g.lda = a.H;
+  g.B = a.w_router;
+  g.ldb = a.H;
+  g.bscale = nullptr;
+  g.K = a.H / S;
+  g.N = E;
+  g.b_rows = E;
+  g.offsets = nullptr;
+  g.E_loc = 1;
+  g.dense_rows = a.T;
+  g.C = a.part;
+  g.ldc = E;
+  g.bias = nullptr;
+  g.n_tiles = (E + kBN - 1) / kBN;
+  g.split_c = a.T * E;
+  const dim3 grid(static_cast<unsigned>(gemm_grid(max_row_tiles(a.T, 1, 32, true), g.n_tiles)), S);
+  if (a.act == MOE_BF16) {
+    hipLaunchKernelGGL((k_gemm_nt<32, 1, 4, MODE_ROUTER, false>), grid, dim3(256), 0, s, g);
+  } else {
+    hipLaunchKernelGGL((k_gemm_nt_f32<MODE_ROUTER>), grid, dim3(256), 0, s, g);
+  }
+  DBOMOE_CHECK_LAUNCH();
+  TopkParams tp{a.part, S, a.T, E, a.bias, a.forced, a.p, a.logits, a.ids, a.w};
+  hipLaunchKernelGGL(k_topk, dim3(static_cast<unsigned>((a.T + 3) / 4)), dim3(256), 0, s, tp);
+  DBOMOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+}  // namespace dbomoe
+
+using namespace dbomoe;
+
+extern "C" size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E) {
+  if (T < 0 || H <= 0 || E <= 0) return 0;
+  return route_ws_bytes(T, H, E);
+}
+
+extern "C" moe_status moe_route_topk(const void* x, moe_dtype act, int64_t T, int32_t H,
+                                     const void* w_router, const float* logit_bias,
+                                     const int32_t* forced_ids, const moe_route_params* params,
+                                     float* logits_out, int32_t* topk_ids, float* topk_w,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_route_params(params);
+  if (st != MOE_OK) return st;
+  if (T < 0 || H <= 0) return MOE_ERR_INVALID_ARG;
+  if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (H % 128) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+      (logit_bias && !aligned16(logit_bias)) || (forced_ids && !aligned16(forced_ids)) ||
+      (logits_out && !aligned16(logits_out)) || !aligned256(ws))
+    return MOE_ERR_MISALIGNED;
+  if (ws_bytes < route_ws_bytes(T, H, params->E)) return MOE_ERR_WORKSPACE;
+  RouteArgs a{x, act, T, H, w_router, logit_bias, forced_ids, *params, logits_out, topk_ids, topk_w,
+              static_cast<float*>(ws)};
+  return launch_route(a, as_stream(stream));
+}

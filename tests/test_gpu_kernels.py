@@ -1,0 +1,261 @@
+"""Per-entry-point GPU parity against the CPU oracle (moe_route_topk,
+moe_dispatch, moe_grouped_ffn, moe_combine), on reduced shapes of the five
+layer configurations and on edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from helpers import assert_close, check_ids, inputs, to_f64, tol_for
+
+pytestmark = pytest.mark.gpu
+
+CIDS = [1, 2, 3, 4, 5]
+
+
+def _gpu():
+    import combine_dual_overlap_amd as C
+    C.binding.lib()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return C
+
+
+def _route(C, cfg, x, w_router, bias=None, forced=None):
+    B = C.binding
+    T = x.shape[0]
+    p = B.route_params(cfg.E, cfg.k, cfg.score, cfg.renormalize, cfg.n_groups, cfg.topk_groups,
+                       cfg.group_topn, cfg.routed_scale)
+    ids = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, cfg.k, dtype=torch.float32, device="cuda")
+    logits = torch.empty(T, cfg.E, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(B.moe_route_workspace_size(T, cfg.H, cfg.E), 256), dtype=torch.uint8, device="cuda")
+    B.moe_route_topk(x, w_router, p, ids, w, ws, logits_out=logits, logit_bias=bias, forced_ids=forced)
+    torch.cuda.synchronize()
+    return ids, w, logits
+
+
+@pytest.mark.parametrize("cid", CIDS)
+def test_route_topk(cid):
+    C = _gpu()
+    inp, ov = inputs(cid, True)
+    cfg = inp["cfg"]
+    dev = lambda t: None if t is None else t.cuda()
+    ids, w, logits = _route(C, cfg, dev(inp["x"]), dev(inp["w_router"]), dev(inp["logit_bias"]),
+                            dev(inp["forced_ids"]))
+    print(f"route cfg={cfg.name} T={cfg.T}", flush=True)
+    ref = O.moe_layer_expert(ov, tokens=np.arange(1))       # routing covers every token
+    gl = to_f64(logits)
+    assert np.abs(gl - ref["logits"]).max() < 1e-4 * max(1.0, np.abs(ref["logits"]).max() / 100)
+    ref_ids, ref_w, diff = check_ids(ids.cpu().numpy(), gl, cfg, ov["forced_ids"])
+    ok = ~diff
+    assert np.abs(w.cpu().double().numpy()[ok] - ref_w[ok]).max() < 1e-5
+    # against the oracle's own float64 routing: identical except at float near-ties
+    mism = (ids.cpu().numpy() != ref["ids"]).any(1).mean()
+    assert mism < 0.01
+
+
+def test_route_ties_pick_lower_index():
+    C = _gpu()
+    cfg = W.LayerConfig("ties", T=8, H=128, E=64, k=4, I=64, act="bf16", wdt="bf16")
+    x = torch.zeros(8, 128, dtype=torch.bfloat16)
+    x[:, 0] = 1.0
+    wr = torch.zeros(64, 128, dtype=torch.bfloat16)
+    wr[[5, 9, 40, 63], 0] = 2.0         # four experts tie at the top
+    wr[[1, 2], 0] = 1.0
+    ids, w, logits = _route(C, cfg, x.cuda(), wr.cuda())
+    assert ids.cpu().tolist() == [[5, 9, 40, 63]] * 8
+    assert torch.allclose(w.cpu(), w.cpu()[:, :1].expand(8, 4))
+
+
+def _dispatch(C, cfg, x, ids, tile_m=16):
+    B = C.binding
+    T = x.shape[0]
+    E_loc = cfg.expert_end - cfg.expert_begin
+    cap = max(T * cfg.k, 1)
+    counts = torch.full((E_loc,), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E_loc + 1,), -7, dtype=torch.int32, device="cuda")
+    toff = torch.full((E_loc + 1,), -7, dtype=torch.int32, device="cuda")
+    perm = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    inv = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    x_perm = torch.zeros(cap, cfg.H, dtype=x.dtype, device="cuda")
+    ws = torch.empty(B.moe_dispatch_workspace_size(T, cfg.k, E_loc), dtype=torch.uint8, device="cuda")
+    B.moe_dispatch(x, ids, cfg.E, cfg.expert_begin, cfg.expert_end, counts, offsets, perm, inv, x_perm, ws,
+                   tile_m=tile_m, tile_offsets=toff)
+    torch.cuda.synchronize()
+    return dict(counts=counts, offsets=offsets, tile_offsets=toff, perm=perm, inv=inv, x_perm=x_perm, ws=ws)
+
+
+def _check_dispatch(cfg, x_cpu, ids_np, g, tile_m=16):
+    ref = O.dispatch_ref(ids_np, cfg.expert_begin, cfg.expert_end, tile_m=tile_m)
+    M = ref["M"]
+    assert np.array_equal(g["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(g["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(g["tile_offsets"].cpu().numpy(), ref["tile_offsets"])
+    assert np.array_equal(g["perm"].cpu().numpy()[:M], ref["perm"])
+    assert np.array_equal(g["inv"].cpu().numpy()[:ids_np.size], ref["inv"])
+    xp = g["x_perm"].cpu()[:M]
+    want = x_cpu[torch.from_numpy(ref["perm"] // cfg.k).long()]
+    assert torch.equal(xp.view(torch.int16) if xp.dtype == torch.bfloat16 else xp.view(torch.int32),
+                       want.view(torch.int16) if want.dtype == torch.bfloat16 else want.view(torch.int32))
+    return ref
+
+
+@pytest.mark.parametrize("cid", CIDS)
+@pytest.mark.parametrize("small", [True, False])
+def test_dispatch(cid, small):
+    C = _gpu()
+    if not small and cid == 4:
+        pytest.skip("the full R1-shaped weights are covered by the layer test")
+    inp, ov = inputs(cid, small)
+    cfg = inp["cfg"]
+    T0 = O.split_point(cfg.T)
+    ids_all = O.moe_layer_expert(ov, tokens=np.arange(1))["ids"]
+    print(f"dispatch cfg={cfg.name} T={cfg.T}", flush=True)
+    for a, b in [(0, T0), (T0, cfg.T)]:
+        x = inp["x"][a:b]
+        ids = ids_all[a:b]
+        g = _dispatch(C, cfg, x.cuda(), torch.from_numpy(ids).cuda())
+        _check_dispatch(cfg, x, ids, g)
+        assert C.binding.moe_get_device_error(g["ws"]) == 0
+
+
+@pytest.mark.parametrize("T,k,E,lo,hi", [(1, 1, 1, 0, 1), (3, 2, 5, 1, 4), (300, 8, 256, 0, 32),
+                                         (257, 6, 64, 0, 64), (64, 16, 300, 100, 300)])
+def test_dispatch_shapes(T, k, E, lo, hi):
+    C = _gpu()
+    rng = np.random.default_rng(T * 31 + k)
+    cfg = W.LayerConfig("d", T=T, H=128, E=E, k=k, I=64, act="bf16", wdt="bf16", expert_begin=lo, expert_end=hi)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = torch.randn(T, 128).to(torch.bfloat16)
+    g = _dispatch(C, cfg, x.cuda(), torch.from_numpy(ids).cuda())
+    _check_dispatch(cfg, x, ids, g)
+
+
+def test_dispatch_all_to_one_expert_and_repeats():
+    C = _gpu()
+    T, k = 700, 4
+    cfg = W.LayerConfig("one", T=T, H=256, E=8, k=k, I=64, act="f32", wdt="f32")
+    ids = np.full((T, k), 3, np.int32)          # repeated ids inside a token are dispatched too
+    x = torch.randn(T, 256)
+    g = _dispatch(C, cfg, x.cuda(), torch.from_numpy(ids).cuda())
+    _check_dispatch(cfg, x, ids, g)
+
+
+def test_dispatch_flags_bad_ids():
+    C = _gpu()
+    cfg = W.LayerConfig("bad", T=10, H=128, E=8, k=2, I=64, act="bf16", wdt="bf16")
+    ids = np.tile(np.array([[1, 2]], np.int32), (10, 1))
+    ids[4, 1] = 8
+    ids[7, 0] = -1
+    x = torch.randn(10, 128).to(torch.bfloat16)
+    g = _dispatch(C, cfg, x.cuda(), torch.from_numpy(ids).cuda())
+    assert C.binding.moe_get_device_error(g["ws"]) == 1
+    inv = g["inv"].cpu().numpy()
+    assert inv[4 * 2 + 1] == -1 and inv[7 * 2 + 0] == -1
+    assert g["offsets"].cpu().numpy()[-1] == 18
+
+
+def test_dispatch_empty_batch():
+    C = _gpu()
+    cfg = W.LayerConfig("empty", T=0, H=128, E=8, k=2, I=64, act="bf16", wdt="bf16")
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device="cuda")
+    g = _dispatch(C, cfg, x, torch.empty(0, 2, dtype=torch.int32, device="cuda"))
+    assert g["counts"].cpu().tolist() == [0] * 8 and g["offsets"].cpu().tolist() == [0] * 9
+
+
+def _ffn(C, x_perm, I, offsets, E_loc, w13, w2, s13=None, s2=None, tile_m=0):
+    B = C.binding
+    cap = x_perm.shape[0]
+    y = torch.full_like(x_perm, float("nan"))
+    ws = torch.empty(max(B.moe_ffn_workspace_size(cap, I, B.dtype_code(x_perm)), 256), dtype=torch.uint8,
+                     device="cuda")
+    B.moe_grouped_ffn(x_perm, I, offsets, E_loc, w13, w2, y, ws, s13, s2, tile_m=tile_m)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("cid", CIDS)
+@pytest.mark.parametrize("tile_m", [0, 32, 64, 128])
+def test_grouped_ffn(cid, tile_m):
+    C = _gpu()
+    inp, ov = inputs(cid, True)
+    cfg = inp["cfg"]
+    if cfg.act == "f32" and tile_m not in (0, 32):
+        pytest.skip("fp32 path has one tile shape")
+    ids = O.moe_layer_expert(ov, tokens=np.arange(1))["ids"]
+    ref = O.dispatch_ref(ids, cfg.expert_begin, cfg.expert_end)
+    M = ref["M"]
+    x_perm = inp["x"][torch.from_numpy(ref["perm"] // cfg.k).long()].contiguous()
+    dev = lambda t: None if t is None else t.cuda()
+    y = _ffn(C, x_perm.cuda(), cfg.I, torch.from_numpy(ref["offsets"]).cuda(), cfg.E_loc, dev(inp["w13"]),
+             dev(inp["w2"]), dev(inp["w13_scale"]), dev(inp["w2_scale"]), tile_m)
+    xp64 = O.decode(W.bits(x_perm), cfg.act)
+    want = O.grouped_ffn_ref(xp64, ref["offsets"], lambda e: O.expert_weights(ov, e))
+    print(f"ffn cfg={cfg.name} M={M} tile_m={tile_m}", flush=True)
+    assert_close(to_f64(y[:M]), want, tol_for(cfg), f"y_perm {cfg.name}")
+
+
+def test_dense_shared_ffn():
+    C = _gpu()
+    inp, ov = inputs(2, True)
+    from combine_dual_overlap_amd.device_layer import concat_shared
+    w13, w2, shI = concat_shared(inp["shared_w13"], inp["shared_w2"])
+    y = _ffn(C, inp["x"].cuda(), shI, None, 1, w13.cuda(), w2.cuda())
+    x64 = O.decode(ov["x"], "bf16")
+    want = sum(O.swiglu_expert(x64, a, b) for a, b in O.shared_weights(ov))
+    assert_close(to_f64(y), want, 1e-2, "shared expert")
+
+
+def test_ffn_single_row_experts_and_gaps():
+    C = _gpu()
+    rng = np.random.default_rng(7)
+    H, I, E = 256, 128, 6
+    counts = np.array([1, 0, 33, 0, 129, 2])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offsets[-1])
+    x = torch.randn(M, H).to(torch.bfloat16)
+    w13 = (torch.randn(E, 2 * I, H) * 0.05).to(torch.bfloat16)
+    w2 = (torch.randn(E, H, I) * 0.05).to(torch.bfloat16)
+    for tm in (32, 64, 128):
+        y = _ffn(C, x.cuda(), I, torch.from_numpy(offsets).cuda(), E, w13.cuda(), w2.cuda(), tile_m=tm)
+        want = O.grouped_ffn_ref(O.decode(W.bits(x), "bf16"), offsets,
+                                 lambda e: (O.decode(W.bits(w13[e]), "bf16"), O.decode(W.bits(w2[e]), "bf16")))
+        assert_close(to_f64(y), want, 1e-2, f"ragged experts tile_m={tm}")
+
+
+@pytest.mark.parametrize("cid", CIDS)
+def test_combine(cid):
+    C = _gpu()
+    inp, ov = inputs(cid, True)
+    cfg = inp["cfg"]
+    r = O.moe_layer_expert(ov, tokens=np.arange(1))
+    ref = O.dispatch_ref(r["ids"], cfg.expert_begin, cfg.expert_end)
+    M, T = ref["M"], cfg.T
+    dt = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    y = torch.randn(max(M, 1), cfg.H).to(dt)
+    shared = torch.randn(T, cfg.H).to(dt) if cfg.n_shared else None
+    w = torch.from_numpy(r["w"].astype(np.float32))
+    out = torch.empty(T, cfg.H, dtype=dt, device="cuda")
+    C.binding.moe_combine(y.cuda(), T, cfg.k, torch.from_numpy(ref["inv"]).cuda(), w.cuda(), out,
+                          shared_out=None if shared is None else shared.cuda())
+    torch.cuda.synchronize()
+    want = O.combine_ref(O.decode(W.bits(y), cfg.act), ref["inv"], w.double().numpy(),
+                         None if shared is None else O.decode(W.bits(shared), cfg.act))
+    assert_close(to_f64(out), want, 4e-3 if cfg.act == "bf16" else 1e-6, f"combine {cfg.name}")
+
+
+def test_invalid_arguments_enqueue_nothing():
+    C = _gpu()
+    B = C.binding
+    x = torch.randn(4, 128, device="cuda").to(torch.bfloat16)
+    ids = torch.zeros(4, 2, dtype=torch.int32, device="cuda")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    t = lambda n: torch.empty(n, dtype=torch.int32, device="cuda")
+    with pytest.raises(B.MoEError) as e:
+        B.moe_dispatch(x, ids, 8, 0, 8, t(8), t(9), t(8), t(8), torch.empty(8, 128, device="cuda",
+                       dtype=torch.bfloat16), small)
+    assert e.value.status == B.MOE_ERR_WORKSPACE
+    with pytest.raises(B.MoEError) as e:
+        B.moe_dispatch(x, ids, 8, 3, 2, t(8), t(9), t(8), t(8), x, small)
+    assert e.value.status == B.MOE_ERR_INVALID_ARG

@@ -1,0 +1,158 @@
+"""Whole-layer GPU parity (dbo_moe_layer) against the CPU oracle: every
+schedule on reduced shapes, the five full-size configurations on sampled
+tokens, split edge cases, DBO == SERIAL bitwise, repeat determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from helpers import assert_close, check_ids, inputs, to_f64, tol_for
+
+pytestmark = pytest.mark.gpu
+
+SCHEDULES = ["unsplit", "serial", "dbo", "dbo_late_event"]
+
+
+def _layer(inp, **kw):
+    import combine_dual_overlap_amd as C
+    C.binding.lib()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return C.DeviceLayer(inp, **kw)
+
+
+def _check_routing_in_workspace(L, cfg, ov, T0):
+    """ids of each microbatch equal the oracle's selection on that
+    microbatch's GPU logits."""
+    halves = [(0, cfg.T)] if T0 is None else [(0, T0), (T0, cfg.T)]
+    for mb, (a, b) in enumerate(halves):
+        n = b - a
+        logits = to_f64(L.view(mb, "logits", torch.float32, (n, cfg.E)))
+        ids = L.view(mb, "topk_ids", torch.int32, (n, cfg.k)).cpu().numpy()
+        forced = None if ov["forced_ids"] is None else ov["forced_ids"][a:b]
+        check_ids(ids, logits, cfg, forced, f"mb{mb} ids")
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_layer_small(cid, schedule):
+    inp, ov = inputs(cid, True)
+    cfg = inp["cfg"]
+    L = _layer(inp)
+    print(f"layer cfg={cfg.name} schedule={schedule}", flush=True)
+    out = L.run(schedule)
+    torch.cuda.synchronize()
+    st = L.ctx.last_stats()
+    T0 = None if schedule == "unsplit" else (cfg.T + 1) // 2
+    assert st["T0"] == (cfg.T if T0 is None else T0)
+    if schedule.startswith("dbo"):
+        assert st["yields_a"] == st["yields_b"] == 3
+    _check_routing_in_workspace(L, cfg, ov, T0)
+    ref = O.moe_layer_expert(ov)
+    assert_close(to_f64(out), ref["out"], tol_for(cfg), f"out {cfg.name} {schedule}")
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_dbo_equals_serial_bitwise_and_repeatable(cid):
+    inp, _ = inputs(cid, True)
+    L = _layer(inp)
+    base = L.run("serial").clone()
+    for sched in ["dbo", "dbo_late_event"] + ["dbo"] * 18:
+        out = L.run(sched)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                           base.view(torch.int16) if base.dtype == torch.bfloat16 else base), sched
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_layer_full_size_sampled(cid):
+    inp, ov = inputs(cid, False)
+    cfg = inp["cfg"]
+    L = _layer(inp)
+    print(f"full layer cfg={cfg.name} T={cfg.T}", flush=True)
+    out = L.run("dbo")
+    torch.cuda.synchronize()
+    T0 = (cfg.T + 1) // 2
+    _check_routing_in_workspace(L, cfg, ov, T0)
+    rng = np.random.default_rng(cid)
+    sample = np.unique(np.concatenate([[0, 1, T0 - 1, T0, T0 + 1, cfg.T - 1], rng.integers(0, cfg.T, 18)]))
+    ref = O.moe_layer_expert(ov, tokens=sample)
+    assert_close(to_f64(out[torch.from_numpy(sample).cuda()]), ref["out"], tol_for(cfg), f"out {cfg.name}")
+    # properties that hold at any size: every dispatched row count adds up
+    for mb, (a, b) in enumerate([(0, T0), (T0, cfg.T)]):
+        E_loc = cfg.E_loc
+        offs = L.view(mb, "offsets", torch.int32, (E_loc + 1,)).cpu().numpy()
+        ids = L.view(mb, "topk_ids", torch.int32, (b - a, cfg.k)).cpu().numpy()
+        local = ((ids >= cfg.expert_begin) & (ids < cfg.expert_end)).sum()
+        assert offs[0] == 0 and offs[-1] == local and (np.diff(offs) >= 0).all()
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 33])
+def test_split_edge_cases(T):
+    cfg = W.get_config(2, small=True).replace(T=T)
+    inp = W.make_inputs(cfg)
+    ov = W.oracle_view(inp)
+    L = _layer(inp)
+    ref = O.moe_layer_expert(ov)
+    for sched in SCHEDULES:
+        out = L.run(sched, min_tokens_to_split=4)
+        torch.cuda.synchronize()
+        st = L.ctx.last_stats()
+        if sched != "unsplit" and T < 4:
+            assert st["schedule"] == 0, "below min_tokens_to_split the layer runs unsplit"
+        assert_close(to_f64(out), ref["out"], 1e-2, f"T={T} {sched}")
+
+
+def test_custom_split_point():
+    inp, ov = inputs(5, True)
+    cfg = inp["cfg"]
+    L = _layer(inp)
+    ref = O.moe_layer_expert(ov)
+    for split_at in [1, 7, cfg.T - 1]:
+        out = L.run("dbo", split_at=split_at)
+        torch.cuda.synchronize()
+        assert L.ctx.last_stats()["T0"] == split_at
+        assert_close(to_f64(out), ref["out"], 1e-2, f"split_at={split_at}")
+
+
+def test_comm_cu_budget_and_tile_override():
+    inp, ov = inputs(3, True)
+    cfg = inp["cfg"]
+    L = _layer(inp)
+    base = L.run("serial").clone()
+    for budget in [1, 8, 64]:
+        out = L.run("dbo", comm_cu_budget=budget)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+    ref = O.moe_layer_expert(ov)
+    for tm in [32, 64, 128]:
+        out = L.run("dbo", ffn_tile_m=tm)
+        torch.cuda.synchronize()
+        assert_close(to_f64(out), ref["out"], tol_for(cfg), f"tile_m={tm}")
+
+
+def test_layer_workspace_too_small_is_rejected():
+    import combine_dual_overlap_amd as C
+    inp, _ = inputs(1, True)
+    L = _layer(inp)
+    small = L.ws[: L.ws.numel() // 2]
+    opts = C.binding.dbo_opts(C.binding.DBO_SCHED_DBO, 2, -1, 0, 0)
+    with pytest.raises(C.binding.MoEError) as e:
+        C.binding.dbo_moe_layer(L.ctx, L.desc, L.x, L.out, opts, small, L.compute, L.comm)
+    assert e.value.status == C.binding.MOE_ERR_WORKSPACE
+
+
+def test_timing_events_report_ffn_times():
+    inp, _ = inputs(2, True)
+    L = _layer(inp)
+    L.ctx.set_timing(True)
+    L.run("dbo")
+    t = L.ctx.ffn_times()
+    assert all(v > 0 for v in t), t
+    L.run("unsplit")
+    t2 = L.ctx.ffn_times()
+    assert t2[0] > 0 and t2[1] > 0 and t2[2:] == [0.0, 0.0]
+    assert L.ctx.ffn_times(1)[2] > 0          # the earlier DBO call is still remembered
+    L.ctx.set_timing(False)
+    L.run("dbo")
+    assert L.ctx.ffn_times() == t2            # untimed calls leave the record alone
