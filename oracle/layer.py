@@ -54,20 +54,28 @@ def _routing(ov: dict):
     return x, logits, ids, w
 
 
-def combine_ref(y_perm: np.ndarray, inv: np.ndarray, w: np.ndarray, shared_out=None) -> np.ndarray:
-    """out[t] = sum_j [inv[t*k+j] >= 0] w[t, j] * y_perm[inv[t*k+j]] (+ shared_out[t])."""
+def combine_ref(y_perm: np.ndarray, inv: np.ndarray, w: np.ndarray, shared_out=None,
+                with_scale: bool = False):
+    """out[t] = sum_j [inv[t*k+j] >= 0] w[t, j] * y_perm[inv[t*k+j]] (+ shared_out[t]).
+
+    with_scale: also return sum_j |w[t, j] * y_perm[...]| (+ |shared_out[t]|),
+    the magnitude of the summed terms."""
     T, k = w.shape
     H = y_perm.shape[1]
     out = np.zeros((T, H), np.float64)
+    scale = np.zeros((T, H), np.float64)
     inv2 = np.asarray(inv).reshape(T, k)
     for t in range(T):
         for j in range(k):
             pos = int(inv2[t, j])
             if pos >= 0:
-                out[t] += float(w[t, j]) * y_perm[pos]
+                term = float(w[t, j]) * y_perm[pos]
+                out[t] += term
+                scale[t] += np.abs(term)
     if shared_out is not None:
         out += shared_out
-    return out
+        scale += np.abs(shared_out)
+    return (out, scale) if with_scale else out
 
 
 def moe_layer_token(ov: dict, tokens=None) -> dict:
@@ -96,23 +104,31 @@ def moe_layer_token(ov: dict, tokens=None) -> dict:
 
 def moe_layer_expert(ov: dict, tokens=None) -> dict:
     """The same layer grouped per expert (one expert's weights decoded at a
-    time, float64 BLAS).  Same return form as moe_layer_token."""
+    time, float64 BLAS).  Same return form as moe_layer_token, plus `scale`:
+    per output element, sum over the token's slots of |w| * (|h| |W2|^T) (and
+    the shared experts' |h| |W2|^T), the magnitude of every term the element
+    sums; |out| <= scale by the triangle inequality."""
     cfg = ov["cfg"]
     x, logits, ids, w = _routing(ov)
     T = x.shape[0]
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     sel_ids = ids[tokens]
     out = np.zeros((len(tokens), cfg.H), np.float64)
+    scale = np.zeros_like(out)
     for el in range(cfg.E_loc):
         rows, slots = np.nonzero(sel_ids == el + cfg.expert_begin)
         if rows.size == 0:
             continue
         w13, w2 = expert_weights(ov, el)
-        y = swiglu_expert(x[tokens[rows]], w13, w2)
-        np.add.at(out, rows, w[tokens[rows], slots][:, None] * y)
+        y, s = swiglu_expert(x[tokens[rows]], w13, w2, with_scale=True)
+        wr = w[tokens[rows], slots][:, None]
+        np.add.at(out, rows, wr * y)
+        np.add.at(scale, rows, np.abs(wr) * s)
     for w13, w2 in shared_weights(ov):
-        out += swiglu_expert(x[tokens], w13, w2)
-    return dict(logits=logits, ids=ids, w=w, out=out, tokens=tokens)
+        y, s = swiglu_expert(x[tokens], w13, w2, with_scale=True)
+        out += y
+        scale += s
+    return dict(logits=logits, ids=ids, w=w, out=out, scale=scale, tokens=tokens)
 
 
 def slice_view(ov: dict, a: int, b: int) -> dict:
@@ -136,8 +152,6 @@ def moe_layer_microbatched(ov: dict, min_tokens_to_split: int = 2, split_at: int
         return r
     ra = layer(slice_view(ov, 0, T0))
     rb = layer(slice_view(ov, T0, T))
-    return dict(logits=np.vstack([ra["logits"], rb["logits"]]),
-                ids=np.vstack([ra["ids"], rb["ids"]]),
-                w=np.vstack([ra["w"], rb["w"]]),
-                out=np.vstack([ra["out"], rb["out"]]),
-                tokens=np.arange(T), T0=T0)
+    r = {key: np.vstack([ra[key], rb[key]]) for key in ("logits", "ids", "w", "out", "scale") if key in ra}
+    r.update(tokens=np.arange(T), T0=T0)
+    return r

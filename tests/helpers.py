@@ -9,10 +9,14 @@ import oracle as O
 from oracle.routing import route_cfg
 import workloads as W
 
-# Tolerances of the floating-point outputs: |gpu - ref| <= tol * (|ref| + rms(ref)).
-# bf16 / fp8-weight values are the ones the layer's statement fixes (1e-2 and
-# 5e-2); the rms term keeps elements near zero from demanding a relative
-# accuracy no bf16 rounding can give.  fp32 (tiny config): 1e-4.
+# Tolerances of the floating-point outputs, relative to the magnitude of what
+# each element sums: |gpu - ref| <= tol * (A + rms(A)/100) with A the oracle's
+# per-element sum of |terms| (for the layer: sum_j |w_j| (|h_j| |W2|^T), plus
+# the shared experts).  The GPU rounds h, y_perm and out to bf16 once each, a
+# first-order error of at most 3 * 2^-9 * A (about 0.6% of A), so the bf16 /
+# fp8-weight tolerances of the layer's statement (1e-2, 5e-2) hold with margin
+# even where the weighted expert outputs cancel; fp32 (tiny config): 1e-4.
+# Without a scale the rule falls back to tol * (|ref| + rms(ref)).
 TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 5e-2}
 
 
@@ -22,20 +26,28 @@ def tol_for(cfg) -> float:
     return TOL["fp8"] if cfg.wdt == "fp8" else TOL["bf16"]
 
 
-def assert_close(gpu, ref, tol, what=""):
+def assert_close(gpu, ref, tol, what="", scale=None):
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     assert np.isfinite(gpu).all(), f"{what}: non-finite values"
-    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     err = np.abs(gpu - ref)
-    bound = tol * (np.abs(ref) + rms)
+    if scale is None:
+        rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+        bound = tol * (np.abs(ref) + rms)
+    else:
+        scale = np.asarray(scale, np.float64)
+        assert (np.abs(ref) <= scale * (1 + 1e-12) + 1e-300).all(), f"{what}: |ref| exceeds its term magnitude"
+        rms = float(np.sqrt(np.mean(scale ** 2))) if scale.size else 0.0
+        bound = tol * (scale + rms / 100)
     bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err / (bound + 1e-300)), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {err.size} outside tol {tol}; worst at {i}: "
-                             f"gpu {gpu[i]!r} ref {ref[i]!r} (rms {rms:.3g}, max abs err {err.max():.3g})")
-    return float(err.max()) if err.size else 0.0
+                             f"gpu {gpu[i]!r} ref {ref[i]!r} bound {bound[i]!r} (max abs err {err.max():.3g})")
+    worst = float((err / (bound / tol + 1e-300)).max()) if err.size else 0.0
+    print(f"  {what}: max abs err {err.max() if err.size else 0:.3g}, worst err/scale {worst:.3g} (tol {tol})")
+    return worst
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
@@ -64,6 +76,28 @@ def grouped_margins(logits: np.ndarray, cfg):
     gs = -np.sort(-g, axis=1)
     gm = gs[:, cfg.topk_groups - 1] - gs[:, cfg.topk_groups]
     return gm
+
+
+def check_routing(gpu_ids, gpu_logits, oracle_logits, cfg, forced=None, what="ids"):
+    """check_ids, plus: the GPU logits equal the oracle's float64 logits to
+    fp32 accuracy, and every row where the oracle's own float64 selection
+    differs from the GPU's is a near-tie (the swapped experts' float64 logits,
+    or for group-limited routing the group scores at the cut, within 2e-4)."""
+    gl = np.asarray(gpu_logits, np.float64)
+    ol = np.asarray(oracle_logits, np.float64)
+    assert (np.abs(gl - ol) <= 1e-4 + 1e-6 * np.abs(ol)).all(), f"{what}: logits differ"
+    check_ids(gpu_ids, gl, cfg, forced, what)
+    own_ids, _ = route_cfg(ol, cfg, forced)
+    gpu_ids = np.asarray(gpu_ids)
+    rows = np.nonzero((own_ids != gpu_ids).any(1))[0]
+    gm = grouped_margins(ol, cfg) if (cfg.score == "sigmoid" and cfg.n_groups > 1) else None
+    for t in rows:
+        j = int(np.nonzero(own_ids[t] != gpu_ids[t])[0][0])
+        a, b = int(gpu_ids[t, j]), int(own_ids[t, j])
+        near = abs(ol[t, a] - ol[t, b]) < 2e-4 or (gm is not None and gm[t] < 2e-4)
+        assert near, f"{what}: token {t} slot {j} picks {a} not {b} away from a near-tie"
+    assert len(rows) <= max(2, 0.01 * len(gpu_ids)), f"{what}: {len(rows)} near-tie rows"
+    return len(rows)
 
 
 def check_ids(gpu_ids, gpu_logits, cfg, forced=None, what="ids"):

@@ -412,3 +412,24 @@ def test_forced_uniform_ids_distinct_and_in_range():
     f = inp["forced_ids"].numpy()
     assert f.shape == (cfg.T, cfg.k) and f.min() >= 0 and f.max() < cfg.E
     assert all(len(set(r)) == cfg.k for r in f)
+
+
+def test_error_scale_bounds_output_and_is_tight_for_nonnegative_terms():
+    cfg = W.LayerConfig("pos", T=12, H=8, E=4, k=2, I=6, act="f32", wdt="f32")
+    x = RNG.uniform(0.1, 1.0, size=(12, 8)).astype(np.float32)
+    wr = RNG.normal(size=(4, 8)).astype(np.float32)
+    w13 = RNG.uniform(0.1, 1.0, size=(4, 12, 8)).astype(np.float32)
+    w2 = RNG.uniform(0.1, 1.0, size=(4, 8, 6)).astype(np.float32)
+    r = O.moe_layer_expert(_tiny_view(cfg, x, wr, w13, w2))
+    assert (r["out"] > 0).all()
+    assert np.allclose(r["scale"], r["out"], rtol=1e-13, atol=0)   # all terms >= 0: |sum| = sum |.|
+    w2n = RNG.normal(size=(4, 8, 6)).astype(np.float32)
+    r2 = O.moe_layer_expert(_tiny_view(cfg, x, wr, w13, w2n))
+    assert (np.abs(r2["out"]) <= r2["scale"] * (1 + 1e-12)).all()
+    assert (np.abs(r2["out"]) < r2["scale"]).any()
+
+
+def test_combine_scale():
+    y = np.array([[1.0, -2.0], [3.0, 4.0]])
+    out, s = O.combine_ref(y, np.array([0, 1]), np.array([[0.5, -1.0]]), with_scale=True)
+    assert np.allclose(out, [[0.5 - 3.0, -1.0 - 4.0]]) and np.allclose(s, [[0.5 + 3.0, 1.0 + 4.0]])
