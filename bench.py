@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--comm-cu-budget", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain elementwise copy of this many MiB three times, the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -125,6 +128,15 @@ def main():
     from combine_dual_overlap_amd import DeviceLayer
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)       # reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"bench: copy calibration, 3 x {args.calibrate_copy_mib} MiB read + write")
     cfg = W.get_config(args.config)
     log(f"bench: generating {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I}")
     inp = W.make_inputs(cfg)
