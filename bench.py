@@ -58,14 +58,16 @@ def read_traffic(workload: str):
         return None
 
 
-def gateup_work(cfg, counts_per_mb):
+def gateup_work(cfg, counts_per_mb, rows_per_mb):
     """Algorithmic bytes and flops of one gate/up GEMM launch per microbatch:
-    weights of every expert that received rows (read once), the dispatched
-    rows (read once), the SwiGLU output h (written once)."""
+    weights of every routed expert that received rows and of the shared
+    experts (each read once), the dispatched rows and the microbatch's rows for
+    the shared experts (read once), the SwiGLU outputs h (written once)."""
     w_s = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
     a_s = 4 if cfg.act == "f32" else 2
+    I_sh = cfg.n_shared * cfg.shared_I
     out = []
-    for counts in counts_per_mb:
+    for counts, T_mb in zip(counts_per_mb, rows_per_mb):
         hit = int((counts > 0).sum())
         M = int(counts.sum())
         wbytes = hit * 2 * cfg.I * cfg.H * w_s
@@ -73,6 +75,9 @@ def gateup_work(cfg, counts_per_mb):
             wbytes += hit * (2 * cfg.I // 128) * (cfg.H // 128) * 4
         nbytes = wbytes + M * cfg.H * a_s + M * cfg.I * a_s
         flops = 2.0 * M * cfg.H * 2 * cfg.I
+        if I_sh:
+            nbytes += 2 * I_sh * cfg.H * a_s + T_mb * cfg.H * a_s + T_mb * I_sh * a_s
+            flops += 2.0 * T_mb * cfg.H * 2 * I_sh
         out.append((nbytes, flops))
     return out
 
@@ -179,7 +184,7 @@ def main():
     T0 = L.ctx.last_stats()["T0"]
     halves = [(0, T0), (T0, T)] if T0 < T else [(0, T)]
     counts = [L.view(mb, "counts", torch.int32, (cfg.E_loc,), T=T).cpu().numpy() for mb in range(len(halves))]
-    work = gateup_work(cfg, counts)
+    work = gateup_work(cfg, counts, [b - a for a, b in halves])
     bytes_launch = float(np.mean([w[0] for w in work]))
     flops_launch = float(np.mean([w[1] for w in work]))
     avg_s = float(np.mean(gu_ms)) / 1e3
@@ -196,7 +201,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                 "frac": round(achieved / mfma_peak, 4)}
     roof["traffic"] = traffic
-    roof["kernel"] = "gate/up expert GEMM + SwiGLU (k_gemm_nt MODE_GATEUP)"
+    roof["kernel"] = "gate/up expert GEMM + SwiGLU, routed and shared experts (k_gemm_nt MODE_GATEUP)"
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
     roof["algorithmic_bytes_per_launch"] = int(bytes_launch)
     roof["algorithmic_flops_per_launch"] = int(flops_launch)

@@ -39,7 +39,8 @@ __device__ __forceinline__ u32x4_t pack_chunk(const float* acc) {
 template <bool BF16, int KMAX, int CH>
 __global__ __launch_bounds__(256) void k_combine(const u32x4_t* __restrict__ y, int64_t T, int row_chunks, int k,
                                                  const int32_t* __restrict__ inv, const float* __restrict__ w,
-                                                 const u32x4_t* __restrict__ shared, u32x4_t* __restrict__ out) {
+                                                 const u32x4_t* __restrict__ shared, int n_shared,
+                                                 u32x4_t* __restrict__ out) {
   constexpr int EPC = BF16 ? 8 : 4;   // elements per 16-byte chunk
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
@@ -83,7 +84,8 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4_t* __restrict__ y, 
       for (int c = 0; c < CH; ++c) {
         const int ci = c0 + c * 64 + lane;
         if (ci < row_chunks) {
-          if (shared) acc_chunk<BF16>(acc[c], shared[t * row_chunks + ci], 1.0f);
+          for (int sl = 0; sl < n_shared; ++sl)
+            acc_chunk<BF16>(acc[c], shared[(sl * T + t) * row_chunks + ci], 1.0f);
           out[t * row_chunks + ci] = pack_chunk<BF16>(acc[c]);
         }
       }
@@ -93,13 +95,13 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4_t* __restrict__ y, 
 
 template <bool BF16>
 static void launch_k(int kmax, dim3 g, hipStream_t s, const u32x4_t* y, int64_t T, int rc, int k,
-                     const int32_t* inv, const float* w, const u32x4_t* sh, u32x4_t* out) {
+                     const int32_t* inv, const float* w, const u32x4_t* sh, int nsh, u32x4_t* out) {
   if (kmax <= 4)
-    hipLaunchKernelGGL((k_combine<BF16, 4, 4>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, out);
+    hipLaunchKernelGGL((k_combine<BF16, 4, 4>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, nsh, out);
   else if (kmax <= 8)
-    hipLaunchKernelGGL((k_combine<BF16, 8, 2>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, out);
+    hipLaunchKernelGGL((k_combine<BF16, 8, 2>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, nsh, out);
   else
-    hipLaunchKernelGGL((k_combine<BF16, 16, 1>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, out);
+    hipLaunchKernelGGL((k_combine<BF16, 16, 1>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, nsh, out);
 }
 
 moe_status launch_combine(const CombineArgs& a, hipStream_t s) {
@@ -111,10 +113,11 @@ moe_status launch_combine(const CombineArgs& a, hipStream_t s) {
   const auto* y = static_cast<const u32x4_t*>(a.y);
   const auto* sh = static_cast<const u32x4_t*>(a.shared);
   auto* out = static_cast<u32x4_t*>(a.out);
+  const int nsh = sh ? (a.n_shared > 0 ? a.n_shared : 1) : 0;
   if (a.act == MOE_BF16)
-    launch_k<true>(a.k, g, s, y, a.T, rc, a.k, a.inv, a.w, sh, out);
+    launch_k<true>(a.k, g, s, y, a.T, rc, a.k, a.inv, a.w, sh, nsh, out);
   else
-    launch_k<false>(a.k, g, s, y, a.T, rc, a.k, a.inv, a.w, sh, out);
+    launch_k<false>(a.k, g, s, y, a.T, rc, a.k, a.inv, a.w, sh, nsh, out);
   DBOMOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -135,6 +138,6 @@ extern "C" moe_status moe_combine(const void* y_perm, moe_dtype act, int64_t T, 
   if (!aligned16(y_perm) || !aligned16(inv) || !aligned16(topk_w) || !aligned16(out) ||
       (shared_out && !aligned16(shared_out)))
     return MOE_ERR_MISALIGNED;
-  CombineArgs a{y_perm, act, T, H, k, inv, topk_w, shared_out, out, 0};
+  CombineArgs a{y_perm, act, T, H, k, inv, topk_w, shared_out, out, 0, shared_out ? 1 : 0};
   return launch_combine(a, as_stream(stream));
 }

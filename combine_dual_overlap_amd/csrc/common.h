@@ -119,15 +119,23 @@ struct FfnArgs {
   const void* w13; const void* w2; moe_dtype wdt; const float* s13; const float* s2;
   void* y; int32_t tile_m; void* h;
   hipEvent_t t0, t1, t2;   // optional timing events around the two GEMMs
+  // Optional dense expert computed in the same launches (the always-on shared
+  // experts): rows1 rows of x1, intermediate size I1, weights in the activation
+  // dtype, output y1 [rows1, H], intermediate h1 [rows1, I1].
+  const void* x1; int64_t rows1; int32_t I1; const void* w13_1; const void* w2_1; void* y1; void* h1;
 };
 moe_status launch_ffn(const FfnArgs& a, hipStream_t s);
 moe_status check_ffn_shapes(moe_dtype act, moe_dtype wdt, int32_t H, int32_t I, int32_t E_loc,
                             const float* s13, const float* s2);
+// K chunks of a dense (shared) expert's down projection run in the grouped
+// launch: each chunk writes its own partial output slab [rows1, H].
+int dense_down_chunks(moe_dtype act, int32_t I1, int32_t I);
 size_t ffn_ws_bytes(int64_t cap_rows, int32_t I, moe_dtype act);
 
 struct CombineArgs {
   const void* y; moe_dtype act; int64_t T; int32_t H; int32_t k;
   const int32_t* inv; const float* w; const void* shared; void* out; int32_t max_blocks;
+  int32_t n_shared;        // slabs [n_shared][T, H] added with weight 1 (1 if shared is set)
 };
 moe_status launch_combine(const CombineArgs& a, hipStream_t s);
 

@@ -15,9 +15,9 @@
 //
 // One host thread issues everything in the order two cooperating microbatch
 // threads would: A.p0, B.p0, A.p1, B.p1, ... with the phases
-//   p0 compute: route [record route-event] [shared expert]   yield
+//   p0 compute: route, record route-event                       yield
 //   p1 comm:    wait route-event, dispatch, record dispatch-event   yield
-//   p2 compute: wait dispatch-event, expert FFN, [record ffn-event]   yield
+//   p2 compute: wait dispatch-event, expert FFN (routed + shared), record ffn-event   yield
 //   p3 comm:    wait ffn-event, combine, record combine-event
 // and finally the compute stream waits both combine events (comm work joined
 // back before anything that follows the layer on the compute stream).
@@ -30,7 +30,7 @@ namespace dbomoe {
 namespace sched {
 
 enum StreamId { kCompute = 0, kComm = 1 };
-enum Stage { kRoute = 0, kShared = 1, kDispatch = 2, kFfn = 3, kCombine = 4, kNumStages = 5 };
+enum Stage { kRoute = 0, kDispatch = 1, kFfn = 2, kCombine = 3, kNumStages = 4 };
 enum Schedule { kUnsplit = 0, kSerial = 1, kDbo = 2, kDboLate = 3 };
 
 struct Op {
@@ -55,9 +55,8 @@ inline Op wait(int s, int mb, int st) { return Op{Op::WAIT, s, mb, st}; }
 inline Op yield(int mb) { return Op{Op::YIELD, -1, mb, -1}; }
 
 // One microbatch, everything in order on the compute stream.
-inline void append_sequential(Plan& p, int mb, bool shared) {
+inline void append_sequential(Plan& p, int mb) {
   p.ops.push_back(launch(kCompute, mb, kRoute));
-  if (shared) p.ops.push_back(launch(kCompute, mb, kShared));
   p.ops.push_back(launch(kCompute, mb, kDispatch));
   p.ops.push_back(launch(kCompute, mb, kFfn));
   p.ops.push_back(launch(kCompute, mb, kCombine));
@@ -66,12 +65,11 @@ inline void append_sequential(Plan& p, int mb, bool shared) {
 // Phase `ph` of microbatch `mb` of the two-stream schedule.  `late`: the
 // compute-stream events that the comm stream waits on are recorded when the
 // microbatch resumes after its yield instead of before it.
-inline void append_phase(Plan& p, int mb, int ph, bool shared, bool late) {
+inline void append_phase(Plan& p, int mb, int ph, bool late) {
   switch (ph) {
     case 0:
       p.ops.push_back(launch(kCompute, mb, kRoute));
       if (!late) p.ops.push_back(record(kCompute, mb, kRoute));
-      if (shared) p.ops.push_back(launch(kCompute, mb, kShared));
       break;
     case 1:
       if (late) p.ops.push_back(record(kCompute, mb, kRoute));
@@ -97,22 +95,22 @@ inline void append_phase(Plan& p, int mb, int ph, bool shared, bool late) {
   }
 }
 
-inline Plan build_plan(int schedule, bool shared) {
+inline Plan build_plan(int schedule) {
   Plan p;
   if (schedule == kUnsplit) {
     p.n_mb = 1;
-    append_sequential(p, 0, shared);
+    append_sequential(p, 0);
     return p;
   }
   p.n_mb = 2;
   if (schedule == kSerial) {
-    append_sequential(p, 0, shared);
-    append_sequential(p, 1, shared);
+    append_sequential(p, 0);
+    append_sequential(p, 1);
     return p;
   }
   const bool late = schedule == kDboLate;
   for (int ph = 0; ph < 4; ++ph)
-    for (int mb = 0; mb < 2; ++mb) append_phase(p, mb, ph, shared, late);
+    for (int mb = 0; mb < 2; ++mb) append_phase(p, mb, ph, late);
   p.ops.push_back(wait(kCompute, 0, kCombine));
   p.ops.push_back(wait(kCompute, 1, kCombine));
   return p;

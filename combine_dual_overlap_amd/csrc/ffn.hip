@@ -5,13 +5,20 @@
 // VLLM" (performance discussion: batched MoE GEMM + act-and-mul).  Reading:
 // W13 = [gate rows 0..I) ; up rows I..2I)], h = silu(gate) * up rounded to the
 // activation dtype, y = h W2^T.
+#include <cmath>
+
 #include "gemm_mfma.h"
 
 namespace dbomoe {
 
-static int choose_tile_m(int64_t rows_hint) {
-  if (rows_hint <= 40) return 32;
-  if (rows_hint <= 96) return 64;
+// Rows per expert under roughly uniform routing are about Poisson(mean): size
+// the row tile for the likely largest expert so an expert's weights stream once
+// (weight-bound decode) and large experts get the big MFMA tile (prefill).
+static int choose_tile_m(int64_t mean_rows) {
+  const double m = static_cast<double>(mean_rows);
+  const double est_max = m + 3.0 * std::sqrt(m) + 1.0;
+  if (est_max <= 32) return 32;
+  if (est_max <= 64) return 64;
   return 128;
 }
 
@@ -25,60 +32,136 @@ static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g) {
     hipLaunchKernelGGL((k_gemm_nt<128, 2, 2, MODE, FP8>), grid, dim3(256), 0, s, g);
 }
 
+static GemmGroup gate_up_group(const void* x, int32_t H, int32_t I, const void* w13, const float* s13, void* h) {
+  GemmGroup g{};
+  g.A = static_cast<const bf16_t*>(x);
+  g.lda = H;
+  g.B = w13;
+  g.ldb = H;
+  g.bscale = s13;
+  g.K = H;
+  g.N = I;
+  g.b_rows = 2 * I;
+  g.n_tiles = I / (kBN / 2);
+  g.C = h;
+  g.ldc = I;
+  g.b_estride = static_cast<int64_t>(g.b_rows) * g.ldb;
+  return g;
+}
+
+static GemmGroup down_group(const void* h, int32_t H, int32_t I, const void* w2, const float* s2, void* y) {
+  GemmGroup g{};
+  g.A = static_cast<const bf16_t*>(h);
+  g.lda = I;
+  g.B = w2;
+  g.ldb = I;
+  g.bscale = s2;
+  g.K = I;
+  g.N = H;
+  g.b_rows = H;
+  g.n_tiles = H / kBN;
+  g.C = y;
+  g.ldc = H;
+  g.b_estride = static_cast<int64_t>(g.b_rows) * g.ldb;
+  return g;
+}
+
+int dense_down_chunks(moe_dtype act, int32_t I1, int32_t I) {
+  if (act == MOE_F32 || I1 <= 0 || I <= 0) return 1;
+  for (int d = (I1 + I - 1) / I; d > 1; --d)
+    if (I1 % (d * kBK) == 0) return d;
+  return 1;
+}
+
+// fp32 path: one SIMT launch per group and GEMM.
+static moe_status launch_ffn_f32(const FfnArgs& a, hipStream_t s) {
+  auto run = [&](const void* x, const int32_t* offsets, int E_loc, int64_t rows, int32_t I, const void* w13,
+                 const void* w2, void* h, void* y) -> moe_status {
+    GemmParams p{};
+    p.offsets = offsets;
+    p.E_loc = E_loc;
+    p.dense_rows = rows;
+    p.g[0] = gate_up_group(x, a.H, I, w13, nullptr, h);
+    const int64_t row_tiles = max_row_tiles(rows, E_loc, 32, offsets == nullptr);
+    hipLaunchKernelGGL(k_gemm_nt_f32<MODE_GATEUP>, dim3(static_cast<unsigned>(gemm_grid(row_tiles * p.g[0].n_tiles))),
+                       dim3(256), 0, s, p);
+    DBOMOE_CHECK_LAUNCH();
+    p.g[0] = down_group(h, a.H, I, w2, nullptr, y);
+    hipLaunchKernelGGL(k_gemm_nt_f32<MODE_DOWN>, dim3(static_cast<unsigned>(gemm_grid(row_tiles * p.g[0].n_tiles))),
+                       dim3(256), 0, s, p);
+    DBOMOE_CHECK_LAUNCH();
+    return MOE_OK;
+  };
+  if (a.t0 && hipEventRecord(a.t0, s) != hipSuccess) return MOE_ERR_HIP;
+  moe_status st = MOE_OK;
+  if (a.cap_rows > 0) st = run(a.x, a.offsets, a.E_loc, a.cap_rows, a.I, a.w13, a.w2, a.h, a.y);
+  if (st == MOE_OK && a.rows1 > 0) st = run(a.x1, nullptr, 1, a.rows1, a.I1, a.w13_1, a.w2_1, a.h1, a.y1);
+  if (st != MOE_OK) return st;
+  if (a.t1 && hipEventRecord(a.t1, s) != hipSuccess) return MOE_ERR_HIP;
+  if (a.t2 && hipEventRecord(a.t2, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+// Worst-case tiles of one grouped GEMM launch (the grid is sized for it;
+// surplus workgroups exit at once).
+static int64_t tiles_max(int bm, int64_t cap_rows, int E_loc, bool dense, int n_tiles0, int64_t rows1, int E1,
+                         int n_tiles1) {
+  const int64_t rt1 = rows1 > 0 ? (rows1 + bm - 1) / bm : 0;
+  const int64_t rt0 = cap_rows > 0 ? max_row_tiles(cap_rows, E_loc, bm, dense) : 0;
+  return rt0 * n_tiles0 + E1 * rt1 * n_tiles1;
+}
+
 moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
-  if (a.cap_rows == 0) return MOE_OK;
-  const bool f32 = a.act == MOE_F32;
+  if (a.cap_rows == 0 && a.rows1 == 0) return MOE_OK;
+  if (a.act == MOE_F32) return launch_ffn_f32(a, s);
   const bool fp8 = a.wdt == MOE_FP8_E4M3FN;
   const bool dense = a.offsets == nullptr;
-  const int bm = f32 ? 32 : (a.tile_m > 0 ? a.tile_m : choose_tile_m(a.rows_hint));
+  const int bm = a.tile_m > 0 ? a.tile_m : choose_tile_m(a.rows_hint);
 
-  GemmParams g1{};
-  g1.A = static_cast<const bf16_t*>(a.x);
-  g1.lda = a.H;
-  g1.B = a.w13;
-  g1.ldb = a.H;
-  g1.bscale = a.s13;
-  g1.K = a.H;
-  g1.N = a.I;
-  g1.b_rows = 2 * a.I;
-  g1.offsets = a.offsets;
-  g1.E_loc = a.E_loc;
-  g1.dense_rows = a.cap_rows;
-  g1.C = a.h;
-  g1.ldc = a.I;
-  g1.n_tiles = a.I / (kBN / 2);
-  const int64_t row_tiles = max_row_tiles(a.cap_rows, a.E_loc, bm, dense);
-  const dim3 grid1(static_cast<unsigned>(gemm_grid(row_tiles, g1.n_tiles)));
-
-  GemmParams g2 = g1;
-  g2.A = static_cast<const bf16_t*>(a.h);
-  g2.lda = a.I;
-  g2.B = a.w2;
-  g2.ldb = a.I;
-  g2.bscale = a.s2;
-  g2.K = a.I;
-  g2.N = a.H;
-  g2.b_rows = a.H;
-  g2.C = a.y;
-  g2.ldc = a.H;
-  g2.n_tiles = a.H / kBN;
-  const dim3 grid2(static_cast<unsigned>(gemm_grid(row_tiles, g2.n_tiles)));
+  GemmParams p1{};
+  p1.offsets = a.offsets;
+  p1.E_loc = a.E_loc;
+  p1.dense_rows = a.cap_rows;
+  p1.rows1 = a.rows1;
+  p1.E1 = 1;
+  p1.g[0] = gate_up_group(a.x, a.H, a.I, a.w13, a.s13, a.h);
+  GemmParams p2 = p1;
+  p2.g[0] = down_group(a.h, a.H, a.I, a.w2, a.s2, a.y);
+  if (a.rows1 > 0) {
+    p1.g[1] = gate_up_group(a.x1, a.H, a.I1, a.w13_1, nullptr, a.h1);
+    // The dense down projection in n_ch K chunks, each a dense expert of the
+    // group writing its own output slab (summed by the combine).
+    const int n_ch = dense_down_chunks(a.act, a.I1, a.I);
+    const int Kc = a.I1 / n_ch;
+    GemmGroup gd = down_group(a.h1, a.H, a.I1, a.w2_1, nullptr, a.y1);
+    gd.K = Kc;
+    gd.a_estride = Kc;
+    gd.b_estride = Kc;
+    gd.c_estride = a.rows1 * a.H;
+    p2.g[1] = gd;
+    p2.E1 = n_ch;
+  }
+  const dim3 grid1(static_cast<unsigned>(gemm_grid(
+      tiles_max(bm, a.cap_rows, a.E_loc, dense, p1.g[0].n_tiles, a.rows1, p1.E1, p1.g[1].n_tiles))));
+  const dim3 grid2(static_cast<unsigned>(gemm_grid(
+      tiles_max(bm, a.cap_rows, a.E_loc, dense, p2.g[0].n_tiles, a.rows1, p2.E1, p2.g[1].n_tiles))));
+  if (a.cap_rows == 0) {   // only the dense group: group 0 keeps no tiles
+    p1.offsets = p2.offsets = nullptr;
+    p1.dense_rows = p2.dense_rows = 0;
+  }
+  const bool fp8_launch = fp8 && a.cap_rows > 0;
 
   if (a.t0 && hipEventRecord(a.t0, s) != hipSuccess) return MOE_ERR_HIP;
-  if (f32)
-    hipLaunchKernelGGL(k_gemm_nt_f32<MODE_GATEUP>, grid1, dim3(256), 0, s, g1);
-  else if (fp8)
-    launch_mfma<MODE_GATEUP, true>(bm, grid1, s, g1);
+  if (fp8_launch)
+    launch_mfma<MODE_GATEUP, true>(bm, grid1, s, p1);
   else
-    launch_mfma<MODE_GATEUP, false>(bm, grid1, s, g1);
+    launch_mfma<MODE_GATEUP, false>(bm, grid1, s, p1);
   DBOMOE_CHECK_LAUNCH();
   if (a.t1 && hipEventRecord(a.t1, s) != hipSuccess) return MOE_ERR_HIP;
-  if (f32)
-    hipLaunchKernelGGL(k_gemm_nt_f32<MODE_DOWN>, grid2, dim3(256), 0, s, g2);
-  else if (fp8)
-    launch_mfma<MODE_DOWN, true>(bm, grid2, s, g2);
+  if (fp8_launch)
+    launch_mfma<MODE_DOWN, true>(bm, grid2, s, p2);
   else
-    launch_mfma<MODE_DOWN, false>(bm, grid2, s, g2);
+    launch_mfma<MODE_DOWN, false>(bm, grid2, s, p2);
   DBOMOE_CHECK_LAUNCH();
   if (a.t2 && hipEventRecord(a.t2, s) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
@@ -137,7 +220,22 @@ extern "C" moe_status moe_grouped_ffn(const void* x_perm, moe_dtype act, int32_t
       (w2_scale && !aligned16(w2_scale)) || !aligned256(ws))
     return MOE_ERR_MISALIGNED;
   if (ws_bytes < ffn_ws_bytes(cap_rows, I, act)) return MOE_ERR_WORKSPACE;
-  FfnArgs a{x_perm, act, H, I, offsets, E_loc, cap_rows, offsets ? cap_rows / E_loc : cap_rows,
-            w13, w2, wdt, w13_scale, w2_scale, y_perm, tile_m, ws, nullptr, nullptr, nullptr};
+  FfnArgs a{};
+  a.x = x_perm;
+  a.act = act;
+  a.H = H;
+  a.I = I;
+  a.offsets = offsets;
+  a.E_loc = E_loc;
+  a.cap_rows = cap_rows;
+  a.rows_hint = offsets ? cap_rows / E_loc : cap_rows;
+  a.w13 = w13;
+  a.w2 = w2;
+  a.wdt = wdt;
+  a.s13 = w13_scale;
+  a.s2 = w2_scale;
+  a.y = y_perm;
+  a.tile_m = tile_m;
+  a.h = ws;
   return launch_ffn(a, as_stream(stream));
 }

@@ -7,20 +7,28 @@
 //  * Row tiles of BM rows per expert (the grouped GEMM's "M tiles"), column
 //    tiles of BN = 128 weight rows; for the gate/up GEMM a column tile holds 64
 //    gate rows and the 64 matching up rows, so SwiGLU is applied in registers.
-//  * Per-expert row counts are on the device: every workgroup rebuilds the
-//    tile map from `offsets` with one wave prefix scan, so the host launches a
-//    worst-case grid and surplus workgroups exit at once.
+//  * A launch covers up to two groups of tiles: group 0 is the routed experts,
+//    whose per-expert row counts live on the device (every workgroup rebuilds
+//    the tile map from `offsets` with one wave prefix scan, so the host launches
+//    a worst-case grid and surplus workgroups exit at once); group 1 is E1 dense
+//    experts over a fixed number of rows (the always-on shared experts, whose
+//    down projection is cut into K chunks with one output slab each), so their
+//    tiles run in the same launch instead of as a small grid of their own.
+//    Group 1 tiles come first in the tile order, so they start with the launch.
 //  * Workgroup b runs on XCD b % 8; the logical tile index is remapped so each
 //    XCD walks a contiguous run of tiles (column tiles of one row tile, then the
 //    next row tile of the same expert), keeping the A rows and the weight tile a
 //    neighbour needs in that XCD's L2.
 //  * 4 waves; each wave owns a WM x WN block made of 16x16 MFMA tiles
-//    (v_mfma_f32_16x16x32_bf16, fp32 accumulators).  K advances 64 per stage;
-//    global loads for stage k+1 are issued before the MFMAs of stage k and land
-//    in the other half of a double-buffered LDS tile (one barrier per stage).
-//  * fp8 e4m3 weights are converted to bf16 once per workgroup on their way to
-//    LDS (exact: every e4m3 value is a bf16 value); the per-128x128-block fp32
-//    scale multiplies the fp32 partial sum of each 128-wide K block.
+//    (v_mfma_f32_16x16x32_bf16, fp32 accumulators).  K advances 64 per stage.
+//    Global loads run two stages ahead of the MFMAs (a two-deep register ring)
+//    and land in a double-buffered LDS tile (one barrier per stage).  LDS rows
+//    are 128 bytes with the 16-byte chunks XOR-swizzled by row, so the 16 rows
+//    an MFMA fragment read touches fall in distinct banks without padding (the
+//    32-row tile then fits four workgroups per CU).
+//  * fp8 e4m3 weights are expanded on their way to LDS: code value times its
+//    128x128 block scale, rounded once to bf16 (the stage's 64-wide K slice lies
+//    in one scale block, and so do the 64 gate or 64 up rows of a tile).
 #pragma once
 
 #include "common.h"
@@ -28,27 +36,40 @@
 namespace dbomoe {
 
 constexpr int kBK = 64;                  // K elements per LDS stage
-constexpr int kLdsStride = kBK + 8;      // bf16 elements per LDS row (16 B pad: spreads banks)
+constexpr int kLdsStride = kBK;          // bf16 elements per LDS row (chunks XOR-swizzled)
 constexpr int kBN = 128;                 // weight rows per column tile
+
+// LDS element offset of 16-byte chunk c (8 bf16) of tile row r.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kLdsStride + ((c ^ (r & 7)) << 3); }
 
 enum GemmMode { MODE_ROUTER = 0, MODE_GATEUP = 1, MODE_DOWN = 2 };
 
-struct GemmParams {
+// One group of tiles: the same K, N and weight layout for every expert in it.
+struct GemmGroup {
   const bf16_t* A;        // activation rows
   int64_t lda;            // elements between rows of A
-  const void* B;          // [E_loc][b_rows][ldb] bf16 or fp8 codes
+  const void* B;          // [experts][b_rows][ldb] bf16 or fp8 codes
   int64_t ldb;            // elements between weight rows
-  const float* bscale;    // fp8: [E_loc][b_rows/128][K/128]
+  const float* bscale;    // fp8: [experts][b_rows/128][K/128], else NULL
   int K;                  // reduction length (multiple of 64; of 128 for fp8)
   int N;                  // output columns: E (router), I (gate/up), H (down)
   int b_rows;             // weight rows per expert
-  const int32_t* offsets; // [E_loc+1] or NULL (dense: one expert with dense_rows rows)
-  int E_loc;
-  int64_t dense_rows;
+  int n_tiles;            // column tiles
   void* C;                // output rows (fp32 for the router, bf16 otherwise)
   int64_t ldc;
-  const float* bias;      // logit bias or NULL (router without split-K only)
-  int n_tiles;            // column tiles
+  // Per-expert element strides of A, B and C (group 1's dense experts: A and
+  // B column offsets of a K chunk, C slab offset); group 0 uses b_estride only.
+  int64_t a_estride, b_estride, c_estride;
+};
+
+struct GemmParams {
+  GemmGroup g[2];
+  const int32_t* offsets; // group 0: [E_loc+1] device offsets, or NULL (one expert of dense_rows rows)
+  int E_loc;
+  int64_t dense_rows;
+  int64_t rows1;          // group 1: rows of each of its dense experts (0 = no group 1)
+  int E1;                 // group 1: number of dense experts
+  const float* bias;      // router logit bias or NULL (unused with split-K)
   int64_t split_c;        // router split-K: blockIdx.y selects K range [y*K, (y+1)*K)
                           // and output slab C + y*split_c
 };
@@ -63,10 +84,14 @@ struct TileShape {
   static_assert(TM >= 1 && TN >= 2 && TN % 2 == 0, "wave tile shape");
 };
 
+struct TileLoc {
+  int grp, e, rows, m_off, nt;
+  int64_t row_begin;
+};
+
 // Locates this workgroup's tile.  Returns false for a surplus workgroup.
 template <int BM>
-__device__ __forceinline__ bool locate_tile(const GemmParams& p, int* s_loc, int& e, int64_t& row_begin,
-                                            int& rows, int& m_off, int& nt) {
+__device__ __forceinline__ bool locate_tile(const GemmParams& p, int* s_loc, TileLoc& t) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     int t4[4];
@@ -84,25 +109,39 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int* s_loc, int
       sum += t4[i];
     }
     const int incl = wave_incl_scan(sum);
-    const int total = __shfl(incl, 63, kWave);
-    const int R = total * p.n_tiles;
+    const int total0 = __shfl(incl, 63, kWave);
+    const int tiles0 = total0 * p.g[0].n_tiles;
+    const int mt1 = static_cast<int>((p.rows1 + BM - 1) / BM);
+    const int tiles1 = p.rows1 > 0 ? p.E1 * mt1 * p.g[1].n_tiles : 0;
+    const int R = tiles1 + tiles0;
     const int per = (R + 7) / 8;
     const int b = blockIdx.x;
     const int L = (b & 7) * per + (b >> 3);
     const bool valid = (b >> 3) < per && L < R;
-    if (lane == 0) s_loc[0] = valid ? 1 : 0;
-    if (valid) {
-      const int mt = L / p.n_tiles;
+    if (lane == 0) {
+      s_loc[0] = valid ? 1 : 0;
+      if (valid && L < tiles1) {    // group 1: dense experts, expert-major
+        const int per_e = mt1 * p.g[1].n_tiles;
+        const int L1 = L % per_e;
+        s_loc[1] = 1;
+        s_loc[2] = L / per_e;
+        s_loc[3] = L1 / p.g[1].n_tiles;
+        s_loc[4] = L1 % p.g[1].n_tiles;
+      }
+    }
+    if (valid && L >= tiles1) {
+      const int L0 = L - tiles1;
+      const int mt = L0 / p.g[0].n_tiles;
       const int excl = incl - sum;
       if (mt >= excl && mt < incl) {
         int acc = excl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (mt >= acc && mt < acc + t4[i]) {
-            const int ex = lane * 4 + i;
-            s_loc[1] = ex;
-            s_loc[2] = mt - acc;
-            s_loc[3] = L % p.n_tiles;
+            s_loc[1] = 0;
+            s_loc[2] = lane * 4 + i;
+            s_loc[3] = mt - acc;
+            s_loc[4] = L0 % p.g[0].n_tiles;
           }
           acc += t4[i];
         }
@@ -111,27 +150,31 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int* s_loc, int
   }
   __syncthreads();
   if (!s_loc[0]) return false;
-  e = s_loc[1];
-  m_off = s_loc[2] * BM;
-  nt = s_loc[3];
-  if (p.offsets) {
-    row_begin = p.offsets[e];
-    rows = p.offsets[e + 1] - p.offsets[e];
+  t.grp = s_loc[1];
+  t.e = s_loc[2];
+  t.m_off = s_loc[3] * BM;
+  t.nt = s_loc[4];
+  if (t.grp == 1) {
+    t.row_begin = 0;
+    t.rows = static_cast<int>(p.rows1);
+  } else if (p.offsets) {
+    t.row_begin = p.offsets[t.e];
+    t.rows = p.offsets[t.e + 1] - p.offsets[t.e];
   } else {
-    row_begin = 0;
-    rows = static_cast<int>(p.dense_rows);
+    t.row_begin = 0;
+    t.rows = static_cast<int>(p.dense_rows);
   }
   return true;
 }
 
 // LDS row of weight tile row r -> weight row inside the expert's matrix.
 template <int MODE>
-__device__ __forceinline__ int b_global_row(const GemmParams& p, int nt, int r) {
+__device__ __forceinline__ int b_global_row(const GemmGroup& g, int nt, int r) {
   if constexpr (MODE == MODE_GATEUP) {
-    return r < kBN / 2 ? nt * (kBN / 2) + r : p.N + nt * (kBN / 2) + (r - kBN / 2);
+    return r < kBN / 2 ? nt * (kBN / 2) + r : g.N + nt * (kBN / 2) + (r - kBN / 2);
   } else if constexpr (MODE == MODE_ROUTER) {
-    const int g = nt * kBN + r;
-    return g < p.N ? g : p.N - 1;
+    const int gr = nt * kBN + r;
+    return gr < g.N ? gr : g.N - 1;
   } else {
     return nt * kBN + r;
   }
@@ -147,22 +190,33 @@ __device__ __forceinline__ int b_lds_row(int wn, int tn) {
   }
 }
 
-__device__ __forceinline__ void fp8x16_to_bf16x16(const u32x4_t& q, u32x4_t& lo, u32x4_t& hi) {
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v[0] = static_cast<__bf16>(a);     // v_cvt_pk_bf16_f32: round to nearest even
+  v[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 16 fp8 e4m3 codes -> 16 bf16 of (code value * s), one rounding each.
+__device__ __forceinline__ void fp8x16_to_bf16x16(const u32x4_t& q, float s, u32x4_t& lo, u32x4_t& hi) {
   uint32_t out[8];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const int v = static_cast<int>(q[w]);
     const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
     const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
-    out[2 * w] = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
-    out[2 * w + 1] = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+    out[2 * w] = cvt_bf16x2(f01[0] * s, f01[1] * s);
+    out[2 * w + 1] = cvt_bf16x2(f23[0] * s, f23[1] * s);
   }
   lo = u32x4_t{out[0], out[1], out[2], out[3]};
   hi = u32x4_t{out[4], out[5], out[6], out[7]};
 }
 
 template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8>
-__global__ __launch_bounds__(256) void k_gemm_nt(GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
+                                          bf16_t (*sA)[BM * kLdsStride], bf16_t (*sB)[kBN * kLdsStride]) {
   using S = TileShape<BM, WAVES_M, WAVES_N>;
   constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
   constexpr int CA = BM * (kBK / 8) / 256;              // 16-byte A chunks per thread
@@ -170,22 +224,15 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams p) {
                          : kBN * (kBK / 8) / 256;
   static_assert(CA >= 1 && CB >= 1, "chunking");
 
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kBN * kLdsStride];
-  __shared__ int s_loc[4];
-
-  int e, rows, m_off, nt;
-  int64_t row_begin;
-  if (!locate_tile<BM>(p, s_loc, e, row_begin, rows, m_off, nt)) return;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
-  const int K = p.K;
+  const int K = g.K;
   const int KT = K / kBK;
   const int64_t ksplit = static_cast<int64_t>(blockIdx.y) * K;   // 0 unless router split-K
+  const int nt = t.nt;
 
   // Global source addresses of this thread's chunks (K offset added per stage).
   const bf16_t* a_src[CA];
@@ -195,37 +242,53 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams p) {
     const int c = tid + i * 256;
     const int r = c / (kBK / 8);
     const int kc = c % (kBK / 8);
-    int mr = m_off + r;
-    mr = mr < rows ? mr : rows - 1;
-    a_src[i] = p.A + (row_begin + mr) * p.lda + ksplit + kc * 8;
-    a_lds[i] = r * kLdsStride + kc * 8;
+    int mr = t.m_off + r;
+    mr = mr < t.rows ? mr : t.rows - 1;
+    a_src[i] = g.A + t.e * g.a_estride + (t.row_begin + mr) * g.lda + ksplit + kc * 8;
+    a_lds[i] = lds_off(r, kc);
   }
-  const size_t expert_elems = static_cast<size_t>(p.b_rows) * p.ldb;
+  const size_t expert_elems = static_cast<size_t>(g.b_estride);
   const uint8_t* b_src[CB];
-  int b_lds[CB];
+  int b_lds[CB], b_lds2[CB];
+  bool b_up[CB];
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int c = tid + i * 256;
+    const int r = FP8 ? c / (kBK / 16) : c / (kBK / 8);
+    const int kc = FP8 ? c % (kBK / 16) : c % (kBK / 8);
+    const int gr = b_global_row<MODE>(g, nt, r);
+    b_up[i] = r >= kBN / 2;
     if constexpr (FP8) {
-      const int r = c / (kBK / 16);
-      const int kc = c % (kBK / 16);
-      const int gr = b_global_row<MODE>(p, nt, r);
-      b_src[i] = static_cast<const uint8_t*>(p.B) + static_cast<size_t>(e) * expert_elems +
-                 static_cast<size_t>(gr) * p.ldb + ksplit + kc * 16;
-      b_lds[i] = r * kLdsStride + kc * 16;
+      b_src[i] = static_cast<const uint8_t*>(g.B) + static_cast<size_t>(t.e) * expert_elems +
+                 static_cast<size_t>(gr) * g.ldb + ksplit + kc * 16;
+      b_lds[i] = lds_off(r, 2 * kc);          // 16 fp8 codes -> two 8-element bf16 chunks
+      b_lds2[i] = lds_off(r, 2 * kc + 1);
     } else {
-      const int r = c / (kBK / 8);
-      const int kc = c % (kBK / 8);
-      const int gr = b_global_row<MODE>(p, nt, r);
-      b_src[i] = reinterpret_cast<const uint8_t*>(static_cast<const bf16_t*>(p.B) +
-                                                  static_cast<size_t>(e) * expert_elems +
-                                                  static_cast<size_t>(gr) * p.ldb + ksplit + kc * 8);
-      b_lds[i] = r * kLdsStride + kc * 8;
+      b_src[i] = reinterpret_cast<const uint8_t*>(static_cast<const bf16_t*>(g.B) +
+                                                  static_cast<size_t>(t.e) * expert_elems +
+                                                  static_cast<size_t>(gr) * g.ldb + ksplit + kc * 8);
+      b_lds[i] = lds_off(r, kc);
+      b_lds2[i] = b_lds[i];
+    }
+  }
+  // fp8 scale rows of this column tile (gate rows / up rows, or the one row block)
+  const float* srow0 = nullptr;
+  const float* srow1 = nullptr;
+  if constexpr (FP8) {
+    const int kblocks = K / 128;
+    const float* se = g.bscale + static_cast<size_t>(t.e) * (g.b_rows / 128) * kblocks;
+    if constexpr (MODE == MODE_GATEUP) {
+      srow0 = se + static_cast<size_t>((nt * (kBN / 2)) / 128) * kblocks;
+      srow1 = se + static_cast<size_t>((g.N + nt * (kBN / 2)) / 128) * kblocks;
+    } else {
+      srow0 = se + static_cast<size_t>((nt * kBN) / 128) * kblocks;
+      srow1 = srow0;
     }
   }
 
-  u32x4_t ra[CA], rb[CB];
-  auto load_stage = [&](int kt) {
+  u32x4_t ra0[CA], rb0[CB], ra1[CA], rb1[CB];
+  float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};
+  auto load_stage = [&](int kt, u32x4_t* ra, u32x4_t* rb, float* sc) {
     const int k0 = kt * kBK;
 #pragma unroll
     for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + k0);
@@ -234,17 +297,21 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams p) {
       const size_t kb = FP8 ? static_cast<size_t>(k0) : static_cast<size_t>(k0) * 2;
       rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + kb);
     }
+    if constexpr (FP8) {
+      sc[0] = srow0[k0 / 128];
+      sc[1] = srow1[k0 / 128];
+    }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf, const u32x4_t* ra, const u32x4_t* rb, const float* sc) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4_t*>(&sA[buf][a_lds[i]]) = ra[i];
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       if constexpr (FP8) {
         u32x4_t lo, hi;
-        fp8x16_to_bf16x16(rb[i], lo, hi);
+        fp8x16_to_bf16x16(rb[i], (MODE == MODE_GATEUP && b_up[i]) ? sc[1] : sc[0], lo, hi);
         *reinterpret_cast<u32x4_t*>(&sB[buf][b_lds[i]]) = lo;
-        *reinterpret_cast<u32x4_t*>(&sB[buf][b_lds[i] + 8]) = hi;
+        *reinterpret_cast<u32x4_t*>(&sB[buf][b_lds2[i]]) = hi;
       } else {
         *reinterpret_cast<u32x4_t*>(&sB[buf][b_lds[i]]) = rb[i];
       }
@@ -252,88 +319,58 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams p) {
   };
 
   f32x4_t acc[TM][TN];
-  f32x4_t part[FP8 ? TM : 1][FP8 ? TN : 1];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if constexpr (FP8) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) part[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // fp8 scale rows of this column tile
-  const float* srow0 = nullptr;
-  const float* srow1 = nullptr;
-  if constexpr (FP8) {
-    const int kblocks = K / 128;
-    const float* se = p.bscale + static_cast<size_t>(e) * (p.b_rows / 128) * kblocks;
-    if constexpr (MODE == MODE_GATEUP) {
-      srow0 = se + static_cast<size_t>((nt * (kBN / 2)) / 128) * kblocks;
-      srow1 = se + static_cast<size_t>((p.N + nt * (kBN / 2)) / 128) * kblocks;
-    } else {
-      srow0 = se + static_cast<size_t>((nt * kBN) / 128) * kblocks;
-      srow1 = srow0;
-    }
-  }
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
 
   const int frag_row = lane & 15;
-  const int frag_k = (lane >> 4) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_stage(kt + 1);
+  const int frag_c = lane >> 4;             // 16-byte chunk within the 32-wide K step
+  auto compute_stage = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
       bf16x8_t af[TM], bfv[TN];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
         af[tm] = *reinterpret_cast<const bf16x8_t*>(
-            &sA[cur][(wm * WM + tm * 16 + frag_row) * kLdsStride + kk * 32 + frag_k]);
+            &sA[buf][lds_off(wm * WM + tm * 16 + frag_row, kk * 4 + frag_c)]);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
         bfv[tn] = *reinterpret_cast<const bf16x8_t*>(
-            &sB[cur][(b_lds_row<MODE, WN, TN>(wn, tn) + frag_row) * kLdsStride + kk * 32 + frag_k]);
+            &sB[buf][lds_off(b_lds_row<MODE, WN, TN>(wn, tn) + frag_row, kk * 4 + frag_c)]);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          if constexpr (FP8)
-            part[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfv[tn], part[tm][tn], 0, 0, 0);
-          else
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfv[tn], acc[tm][tn], 0, 0, 0);
-        }
+        for (int tn = 0; tn < TN; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfv[tn], acc[tm][tn], 0, 0, 0);
     }
-    if constexpr (FP8) {
-      if (kt & 1) {
-        const int kb = kt >> 1;
-        const float s0 = srow0[kb];
-        const float s1 = srow1[kb];
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            const float s = (MODE == MODE_GATEUP && tn >= TN / 2) ? s1 : s0;
-            acc[tm][tn] += s * part[tm][tn];
-            part[tm][tn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-      }
-    }
-    if (kt + 1 < KT) store_stage(cur ^ 1);
+  };
+
+  // Two-deep register ring: stage s is loaded into ring slot s % 2 two stages
+  // before its MFMAs and stored to LDS buffer s % 2 one stage before them.
+  load_stage(0, ra0, rb0, sc0);
+  if (KT > 1) load_stage(1, ra1, rb1, sc1);
+  store_stage(0, ra0, rb0, sc0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    if (kt + 2 < KT) load_stage(kt + 2, ra0, rb0, sc0);
+    compute_stage(0);
+    store_stage(1, ra1, rb1, sc1);
+    __syncthreads();
+    if (kt + 3 < KT) load_stage(kt + 3, ra1, rb1, sc1);
+    compute_stage(1);
+    if (kt + 2 < KT) store_stage(0, ra0, rb0, sc0);
     __syncthreads();
   }
+  if (kt < KT) compute_stage(0);
 
   // Epilogue.  Accumulator element r of lane l in a 16x16 tile is
   // (row 4*(l/16) + r, column l%16).
   const int col_in = lane & 15;
   const int row_q = (lane >> 4) * 4;
   if constexpr (MODE == MODE_GATEUP) {
-    bf16_t* C = static_cast<bf16_t*>(p.C);
+    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -341,16 +378,16 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams p) {
         const int col = nt * (kBN / 2) + wn * (WN / 2) + tn * 16 + col_in;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int mr = m_off + wm * WM + tm * 16 + row_q + r;
-          if (mr < rows) {
-            const float g = acc[tm][tn][r];
+          const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
+          if (mr < t.rows) {
+            const float gt = acc[tm][tn][r];
             const float u = acc[tm][tn + TN / 2][r];
-            C[(row_begin + mr) * p.ldc + col] = f32_to_bf16(silu_f32(g) * u);
+            C[(t.row_begin + mr) * g.ldc + col] = f32_to_bf16(silu_f32(gt) * u);
           }
         }
       }
   } else if constexpr (MODE == MODE_DOWN) {
-    bf16_t* C = static_cast<bf16_t*>(p.C);
+    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -358,27 +395,45 @@ __global__ __launch_bounds__(256) void k_gemm_nt(GemmParams p) {
         const int col = nt * kBN + wn * WN + tn * 16 + col_in;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int mr = m_off + wm * WM + tm * 16 + row_q + r;
-          if (mr < rows) C[(row_begin + mr) * p.ldc + col] = f32_to_bf16(acc[tm][tn][r]);
+          const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
+          if (mr < t.rows) C[(t.row_begin + mr) * g.ldc + col] = f32_to_bf16(acc[tm][tn][r]);
         }
       }
   } else {
-    float* C = static_cast<float*>(p.C) + blockIdx.y * p.split_c;
+    float* C = static_cast<float*>(g.C) + blockIdx.y * p.split_c;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         const int col = nt * kBN + wn * WN + tn * 16 + col_in;
-        if (col < p.N) {
+        if (col < g.N) {
           const float b = p.bias ? p.bias[col] : 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int mr = m_off + wm * WM + tm * 16 + row_q + r;
-            if (mr < rows) C[(row_begin + mr) * p.ldc + col] = acc[tm][tn][r] + b;
+            const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
+            if (mr < t.rows) C[(t.row_begin + mr) * g.ldc + col] = acc[tm][tn][r] + b;
           }
         }
       }
   }
+}
+
+// Waves per SIMD each tile shape is built for: 4 for the 32-row tile (40 KB of
+// LDS, so four workgroups share a CU), 3 for 64 rows, 2 for 128 rows.
+template <int BM> struct MinWaves { static constexpr int value = BM == 32 ? 4 : BM == 64 ? 3 : 2; };
+
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8>
+__global__ __launch_bounds__(256, MinWaves<BM>::value) void k_gemm_nt(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * kLdsStride];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kBN * kLdsStride];
+  int* s_loc = reinterpret_cast<int*>(&sA[0][0]);   // tile location, before sA holds A tiles
+  TileLoc t;
+  if (!locate_tile<BM>(p, s_loc, t)) return;
+  __syncthreads();                                  // s_loc read by all before sA is filled
+  if (FP8 && t.grp == 0)
+    gemm_tile<BM, WAVES_M, WAVES_N, MODE, FP8>(p.g[0], t, p, sA, sB);
+  else
+    gemm_tile<BM, WAVES_M, WAVES_N, MODE, false>(p.g[t.grp], t, p, sA, sB);
 }
 
 // Worst-case number of row tiles: sum_e ceil(n_e / BM) <= ceil(cap / BM) + E_loc.
@@ -387,49 +442,47 @@ inline int64_t max_row_tiles(int64_t cap_rows, int E_loc, int BM, bool dense) {
   return (cap_rows + BM - 1) / BM + E_loc;
 }
 
-inline int64_t gemm_grid(int64_t row_tiles, int n_tiles) {
-  const int64_t g = row_tiles * n_tiles;
-  return (g + 7) / 8 * 8;
-}
+inline int64_t gemm_grid(int64_t tiles) { return (tiles + 7) / 8 * 8; }
 
-// fp32 SIMT variant of the same tiling (fp32 activations and weights only):
-// 32 rows x 128 weight rows per workgroup, K staged 32 at a time through LDS,
-// each thread owns 2 rows x 8 columns (gate/up: 2 rows x 4 gate + 4 up columns).
+// fp32 SIMT variant of the same tiling (fp32 activations and weights only, one
+// group per launch): 32 rows x 128 weight rows per workgroup, K staged 32 at a
+// time through LDS, each thread owns 2 rows x 8 columns (gate/up: 2 rows x 4
+// gate + 4 up columns).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_gemm_nt_f32(GemmParams p) {
   constexpr int BM = 32, BKF = 32;
   __shared__ float sA[BM][BKF + 1];
   __shared__ float sB[kBN][BKF + 1];
-  __shared__ int s_loc[4];
-  int e, rows, m_off, nt;
-  int64_t row_begin;
-  if (!locate_tile<BM>(p, s_loc, e, row_begin, rows, m_off, nt)) return;
+  __shared__ int s_loc[8];
+  TileLoc t;
+  if (!locate_tile<BM>(p, s_loc, t)) return;
+  const GemmGroup& g = p.g[0];
 
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  const int64_t ksplit = static_cast<int64_t>(blockIdx.y) * p.K;
-  const float* A = reinterpret_cast<const float*>(p.A) + ksplit;
-  const float* B = static_cast<const float*>(p.B) + static_cast<size_t>(e) * p.b_rows * p.ldb + ksplit;
+  const int64_t ksplit = static_cast<int64_t>(blockIdx.y) * g.K;
+  const float* A = reinterpret_cast<const float*>(g.A) + ksplit;
+  const float* B = static_cast<const float*>(g.B) + static_cast<size_t>(t.e) * g.b_estride + ksplit;
   float acc[2][8];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
 
-  for (int k0 = 0; k0 < p.K; k0 += BKF) {
+  for (int k0 = 0; k0 < g.K; k0 += BKF) {
 #pragma unroll
     for (int i = 0; i < BM * BKF / 256; ++i) {
       const int c = tid + i * 256;
       const int r = c / BKF, kc = c % BKF;
-      int mr = m_off + r;
-      mr = mr < rows ? mr : rows - 1;
-      sA[r][kc] = A[(row_begin + mr) * p.lda + k0 + kc];
+      int mr = t.m_off + r;
+      mr = mr < t.rows ? mr : t.rows - 1;
+      sA[r][kc] = A[(t.row_begin + mr) * g.lda + k0 + kc];
     }
 #pragma unroll
     for (int i = 0; i < kBN * BKF / 256; ++i) {
       const int c = tid + i * 256;
       const int r = c / BKF, kc = c % BKF;
-      sB[r][kc] = B[static_cast<size_t>(b_global_row<MODE>(p, nt, r)) * p.ldb + k0 + kc];
+      sB[r][kc] = B[static_cast<size_t>(b_global_row<MODE>(g, t.nt, r)) * g.ldb + k0 + kc];
     }
     __syncthreads();
 #pragma unroll 4
@@ -449,20 +502,20 @@ __global__ __launch_bounds__(256) void k_gemm_nt_f32(GemmParams p) {
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int mr = m_off + ty + 16 * i;
-    if (mr >= rows) continue;
-    float* C = static_cast<float*>(p.C) + blockIdx.y * p.split_c + (row_begin + mr) * p.ldc;
+    const int mr = t.m_off + ty + 16 * i;
+    if (mr >= t.rows) continue;
+    float* C = static_cast<float*>(g.C) + blockIdx.y * p.split_c + (t.row_begin + mr) * g.ldc;
     if constexpr (MODE == MODE_GATEUP) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float g = acc[i][j], u = acc[i][j + 4];
-        C[nt * (kBN / 2) + tx + 16 * j] = g / (1.0f + expf(-g)) * u;
+        const float gt = acc[i][j], u = acc[i][j + 4];
+        C[t.nt * (kBN / 2) + tx + 16 * j] = gt / (1.0f + expf(-gt)) * u;
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int col = nt * kBN + tx + 16 * j;
-        if (MODE == MODE_ROUTER && col >= p.N) continue;
+        const int col = t.nt * kBN + tx + 16 * j;
+        if (MODE == MODE_ROUTER && col >= g.N) continue;
         C[col] = acc[i][j] + ((MODE == MODE_ROUTER && p.bias) ? p.bias[col] : 0.f);
       }
     }

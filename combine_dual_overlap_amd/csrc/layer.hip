@@ -65,7 +65,9 @@ HalfLayout half_layout(const moe_layer_desc* d, int64_t T) {
   sz[B_INV] = static_cast<size_t>(cap) * 4;
   sz[B_XPERM] = static_cast<size_t>(cap) * d->H * as;
   sz[B_YPERM] = static_cast<size_t>(cap) * d->H * as;
-  sz[B_SHOUT] = d->shared_I > 0 ? static_cast<size_t>(T) * d->H * as : 0;
+  sz[B_SHOUT] = d->shared_I > 0
+                    ? static_cast<size_t>(dense_down_chunks(d->act, d->shared_I, d->I)) * T * d->H * as
+                    : 0;
   sz[B_DISPWS] = dispatch_ws_bytes(T, k, E_loc);
   sz[B_ROUTEWS] = route_ws_bound(T, E);
   sz[B_H] = ffn_ws_bytes(cap, d->I, d->act);
@@ -140,13 +142,6 @@ struct HipBackend {
         st = launch_route(a, s);
         break;
       }
-      case sched::kShared: {
-        FfnArgs a{xm, d->act, d->H, d->shared_I, nullptr, 1, T, T, d->shared_w13, d->shared_w2, d->act,
-                  nullptr, nullptr, buf<void>(mb, B_SHOUT), o->ffn_tile_m, buf<void>(mb, B_SHH),
-                  nullptr, nullptr, nullptr};
-        st = launch_ffn(a, s);
-        break;
-      }
       case sched::kDispatch: {
         DispatchArgs a{xm, d->act, T, d->H, buf<int32_t>(mb, B_IDS), k, d->route.E, d->expert_begin,
                        d->expert_end, 0, buf<int32_t>(mb, B_COUNTS), buf<int32_t>(mb, B_OFFSETS),
@@ -156,10 +151,35 @@ struct HipBackend {
         break;
       }
       case sched::kFfn: {
+        // Routed experts on the dispatched rows plus the shared experts on the
+        // microbatch's own rows, in the same two launches.
         const int64_t hint = (T * k + d->route.E - 1) / d->route.E;
-        FfnArgs a{buf<void>(mb, B_XPERM), d->act, d->H, d->I, buf<int32_t>(mb, B_OFFSETS), E_loc, T * k, hint,
-                  d->w13, d->w2, d->wdt, d->w13_scale, d->w2_scale, buf<void>(mb, B_YPERM), o->ffn_tile_m,
-                  buf<void>(mb, B_H), nullptr, nullptr, nullptr};
+        FfnArgs a{};
+        a.x = buf<void>(mb, B_XPERM);
+        a.act = d->act;
+        a.H = d->H;
+        a.I = d->I;
+        a.offsets = buf<int32_t>(mb, B_OFFSETS);
+        a.E_loc = E_loc;
+        a.cap_rows = T * k;
+        a.rows_hint = hint;
+        a.w13 = d->w13;
+        a.w2 = d->w2;
+        a.wdt = d->wdt;
+        a.s13 = d->w13_scale;
+        a.s2 = d->w2_scale;
+        a.y = buf<void>(mb, B_YPERM);
+        a.tile_m = o->ffn_tile_m;
+        a.h = buf<void>(mb, B_H);
+        if (d->shared_I > 0) {
+          a.x1 = xm;
+          a.rows1 = T;
+          a.I1 = d->shared_I;
+          a.w13_1 = d->shared_w13;
+          a.w2_1 = d->shared_w2;
+          a.y1 = buf<void>(mb, B_SHOUT);
+          a.h1 = buf<void>(mb, B_SHH);
+        }
         if (ctx->timing) {
           a.t0 = ctx->tev[ctx->slot][mb][0];
           a.t1 = ctx->tev[ctx->slot][mb][1];
@@ -172,7 +192,7 @@ struct HipBackend {
       case sched::kCombine: {
         CombineArgs a{buf<void>(mb, B_YPERM), d->act, T, d->H, k, buf<int32_t>(mb, B_INV), buf<float>(mb, B_W),
                       d->shared_I > 0 ? buf<void>(mb, B_SHOUT) : nullptr, out + row0[mb] * d->H * as,
-                      o->comm_cu_budget};
+                      o->comm_cu_budget, d->shared_I > 0 ? dense_down_chunks(d->act, d->shared_I, d->I) : 0};
         st = launch_combine(a, s);
         break;
       }
@@ -212,9 +232,12 @@ extern "C" moe_status dbo_ctx_create(dbo_ctx** ctx) {
   if (!ctx) return MOE_ERR_INVALID_ARG;
   dbo_ctx* c = new dbo_ctx();
   bool ok = true;
+  // The schedule's events only order two streams of one device: no host wait
+  // ever synchronises on them, so they skip the system-scope fence.
+  const unsigned flags = hipEventDisableTiming | hipEventDisableSystemFence;
   for (int i = 0; i < sched::kNumEvents; ++i)
-    ok = ok && hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming) == hipSuccess;
-  ok = ok && hipEventCreateWithFlags(&c->join, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&c->ev[i], flags) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&c->join, flags) == hipSuccess;
   if (!ok) {
     dbo_ctx_destroy(c);
     return MOE_ERR_HIP;
@@ -347,7 +370,7 @@ extern "C" moe_status dbo_moe_layer(dbo_ctx* ctx, const moe_layer_desc* d, const
     ctx->timed[ctx->slot][0] = ctx->timed[ctx->slot][1] = false;
     ctx->timed_calls++;
   }
-  const sched::Plan plan = sched::build_plan(schedule, d->shared_I > 0);
+  const sched::Plan plan = sched::build_plan(schedule);
   sched::RunStats rs;
   const int r = sched::run_plan(plan, be, &rs);
   ctx->stats[0] = schedule;

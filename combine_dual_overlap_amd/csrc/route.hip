@@ -202,7 +202,8 @@ moe_status launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return MOE_OK;
   const int E = a.p.E;
   const int S = route_splits(a.T, a.H, E);
-  GemmParams g{};
+  GemmParams p{};
+  GemmGroup& g = p.g[0];
   g.A = static_cast<const bf16_t*>(a.x);
   g.lda = a.H;
   g.B = a.w_router;
@@ -211,19 +212,21 @@ moe_status launch_route(const RouteArgs& a, hipStream_t s) {
   g.K = a.H / S;
   g.N = E;
   g.b_rows = E;
-  g.offsets = nullptr;
-  g.E_loc = 1;
-  g.dense_rows = a.T;
+  g.n_tiles = (E + kBN - 1) / kBN;
   g.C = a.part;
   g.ldc = E;
-  g.bias = nullptr;
-  g.n_tiles = (E + kBN - 1) / kBN;
-  g.split_c = a.T * E;
-  const dim3 grid(static_cast<unsigned>(gemm_grid(max_row_tiles(a.T, 1, 32, true), g.n_tiles)), S);
+  g.b_estride = static_cast<int64_t>(E) * a.H;
+  p.offsets = nullptr;
+  p.E_loc = 1;
+  p.dense_rows = a.T;
+  p.rows1 = 0;
+  p.bias = nullptr;
+  p.split_c = a.T * E;
+  const dim3 grid(static_cast<unsigned>(gemm_grid(max_row_tiles(a.T, 1, 32, true) * g.n_tiles)), S);
   if (a.act == MOE_BF16) {
-    hipLaunchKernelGGL((k_gemm_nt<32, 1, 4, MODE_ROUTER, false>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_gemm_nt<32, 1, 4, MODE_ROUTER, false>), grid, dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_gemm_nt_f32<MODE_ROUTER>), grid, dim3(256), 0, s, g);
+    hipLaunchKernelGGL((k_gemm_nt_f32<MODE_ROUTER>), grid, dim3(256), 0, s, p);
   }
   DBOMOE_CHECK_LAUNCH();
   TopkParams tp{a.part, S, a.T, E, a.bias, a.forced, a.p, a.logits, a.ids, a.w};

@@ -143,6 +143,8 @@ moe_status moe_get_device_error(const void* dispatch_ws, int32_t* code, void* st
  *   tile_m   0 = automatic; else 32, 64 or 128 rows per MFMA tile
  *   ws       moe_ffn_workspace_size(cap_rows, I, act) bytes (holds h)
  * H % 128 == 0 and I % 64 == 0 (fp8: I % 128 == 0), else MOE_ERR_UNSUPPORTED.
+ * fp8 weights are expanded to bf16 (code value x block scale, rounded once) on
+ * their way to the MFMA tiles.
  * ------------------------------------------------------------------------- */
 size_t moe_ffn_workspace_size(int64_t cap_rows, int32_t I, moe_dtype act);
 moe_status moe_grouped_ffn(const void* x_perm, moe_dtype act, int32_t H, int32_t I,

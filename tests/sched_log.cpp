@@ -1,6 +1,6 @@
 // Host-only driver of the DBO schedule (dbo_schedule.h) on a recording
 // backend: prints every operation the schedule issues so the Python test can
-// rebuild the happens-before graph.  Usage: sched_log <schedule> <shared 0|1> <fail_at|-1>
+// rebuild the happens-before graph.  Usage: sched_log <schedule> <fail_at|-1>
 #include <cstdio>
 #include <cstdlib>
 
@@ -34,12 +34,11 @@ struct Recorder {
 };
 
 int main(int argc, char** argv) {
-  if (argc < 4) return 2;
+  if (argc < 3) return 2;
   const int schedule = std::atoi(argv[1]);
-  const bool shared = std::atoi(argv[2]) != 0;
   Recorder rec;
-  rec.fail_at = std::atoi(argv[3]);
-  const Plan plan = build_plan(schedule, shared);
+  rec.fail_at = std::atoi(argv[2]);
+  const Plan plan = build_plan(schedule);
   RunStats st;
   const int status = run_plan(plan, rec, &st);
   std::printf("YIELDS %d %d\n", st.yields[0], st.yields[1]);

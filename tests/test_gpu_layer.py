@@ -128,8 +128,9 @@ def test_custom_split_point():
         assert_close(to_f64(out), ref["out"], 1e-2, f"split_at={split_at}", ref["scale"])
 
 
-def test_comm_cu_budget_and_tile_override():
-    inp, ov = inputs(3, True)
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_comm_cu_budget_and_tile_overrides(cid):
+    inp, ov = inputs(cid, True)
     cfg = inp["cfg"]
     L = _layer(inp)
     base = L.run("serial").clone()
@@ -139,9 +140,12 @@ def test_comm_cu_budget_and_tile_override():
         assert torch.equal(out.view(torch.int16), base.view(torch.int16))
     ref = O.moe_layer_expert(ov)
     for tm in [32, 64, 128]:
-        out = L.run("dbo", ffn_tile_m=tm)
+        out = L.run("dbo", ffn_tile_m=tm).clone()
         torch.cuda.synchronize()
         assert_close(to_f64(out), ref["out"], tol_for(cfg), f"tile_m={tm}", ref["scale"])
+        again = L.run("serial", ffn_tile_m=tm).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), again.view(torch.int16))
 
 
 def test_layer_workspace_too_small_is_rejected():

@@ -92,6 +92,9 @@ def test_entry_points_reject_bad_arguments_without_a_device():
     # fp32 activations with bf16 weights
     assert L.moe_grouped_ffn(A, B.MOE_F32, 256, 192, A, 4, 100, A, A, B.MOE_BF16, None, None, A, 0, A,
                              1 << 30, None) == B.MOE_ERR_UNSUPPORTED
+    # tile height out of range
+    assert L.moe_grouped_ffn(A, B.MOE_BF16, 256, 192, A, 4, 100, A, A, B.MOE_BF16, None, None, A, 48, A,
+                             1 << 30, None) == B.MOE_ERR_INVALID_ARG
     # combine: out aliasing y_perm
     assert L.moe_combine(A, B.MOE_BF16, 4, 128, 2, A, A, None, A, None) == B.MOE_ERR_INVALID_ARG
     # route: group-limited with k larger than the kept groups hold

@@ -25,9 +25,9 @@ import pytest
 from conftest import ROOT
 
 SCHED = {"unsplit": 0, "serial": 1, "dbo": 2, "late": 3}
-ROUTE, SHARED, DISPATCH, FFN, COMBINE = range(5)
+ROUTE, DISPATCH, FFN, COMBINE = range(4)
 COMPUTE, COMM = 0, 1
-NAMES = ["route", "shared", "dispatch", "ffn", "combine"]
+NAMES = ["route", "dispatch", "ffn", "combine"]
 
 
 @pytest.fixture(scope="module")
@@ -39,9 +39,8 @@ def sched_bin(tmp_path_factory):
     return out
 
 
-def run_log(binary, schedule, shared, fail_at=-1):
-    r = subprocess.run([binary, str(SCHED[schedule]), str(int(shared)), str(fail_at)], capture_output=True,
-                       text=True, check=True)
+def run_log(binary, schedule, fail_at=-1):
+    r = subprocess.run([binary, str(SCHED[schedule]), str(fail_at)], capture_output=True, text=True, check=True)
     ops = []
     status = yields = None
     for line in r.stdout.splitlines():
@@ -115,14 +114,15 @@ class Graph:
 
 
 def accesses(mb, stage, half):
-    """Buffers one stage's kernels read and write (half = workspace half)."""
+    """Buffers one stage's kernels read and write (half = workspace half).
+    The FFN stage also runs the shared experts on the microbatch's rows."""
     h = f"ws{half}"
     table = {
         ROUTE: ({f"x{mb}", "w_router"}, {f"{h}.logits", f"{h}.ids", f"{h}.w", f"{h}.route_ws"}),
-        SHARED: ({f"x{mb}", "w_shared"}, {f"{h}.shared_h", f"{h}.shared_out"}),
         DISPATCH: ({f"x{mb}", f"{h}.ids"}, {f"{h}.counts", f"{h}.offsets", f"{h}.perm", f"{h}.inv",
                                            f"{h}.x_perm", f"{h}.disp_ws"}),
-        FFN: ({f"{h}.x_perm", f"{h}.offsets", "w13", "w2"}, {f"{h}.h", f"{h}.y"}),
+        FFN: ({f"{h}.x_perm", f"{h}.offsets", "w13", "w2", f"x{mb}", "w_shared"},
+              {f"{h}.h", f"{h}.y", f"{h}.shared_h", f"{h}.shared_out"}),
         COMBINE: ({f"{h}.y", f"{h}.inv", f"{h}.w", f"{h}.shared_out"}, {f"out{mb}"}),
     }
     return table[stage]
@@ -142,55 +142,47 @@ def races(g, halves=(0, 1)):
     return found
 
 
-@pytest.mark.parametrize("shared", [False, True])
 @pytest.mark.parametrize("schedule", ["dbo", "late", "serial", "unsplit"])
-def test_schedule_invariants(sched_bin, schedule, shared):
-    ops, status, yields = run_log(sched_bin, schedule, shared)
+def test_schedule_invariants(sched_bin, schedule):
+    ops, status, yields = run_log(sched_bin, schedule)
     assert status == 0
     g = Graph(ops)
     assert g.wait_ok
     n_mb = 1 if schedule == "unsplit" else 2
-    stages = [ROUTE, SHARED, DISPATCH, FFN, COMBINE] if shared else [ROUTE, DISPATCH, FFN, COMBINE]
+    stages = [ROUTE, DISPATCH, FFN, COMBINE]
     assert sorted(g.launch) == sorted((mb, st) for mb in range(n_mb) for st in stages)
     if schedule in ("dbo", "late"):
         assert yields == (3, 3)
     # each microbatch's own chain is ordered, and the layer ends after both combines
     for mb in range(n_mb):
-        chain = [g.node(mb, st) for st in (ROUTE, DISPATCH, FFN, COMBINE)]
+        chain = [g.node(mb, st) for st in stages]
         for a, b in zip(chain, chain[1:]):
             assert g.before(a, b), (schedule, mb)
-        if shared:
-            assert g.before(g.node(mb, ROUTE), g.node(mb, SHARED))
-            assert g.before(g.node(mb, SHARED), g.node(mb, COMBINE))
         assert g.before(g.node(mb, COMBINE), "END")
     assert races(g) == []
 
 
-@pytest.mark.parametrize("shared", [False, True])
-def test_event_before_yield_removes_cross_microbatch_waits(sched_bin, shared):
-    g = Graph(run_log(sched_bin, "dbo", shared)[0])
+def test_event_before_yield_removes_cross_microbatch_waits(sched_bin):
+    g = Graph(run_log(sched_bin, "dbo")[0])
     A, B = 0, 1
     # A's comm waits only on A's compute tail
     assert not g.before(g.node(B, ROUTE), g.node(A, DISPATCH))
     assert not g.before(g.node(B, FFN), g.node(A, COMBINE))
-    if shared:
-        assert not g.before(g.node(A, SHARED), g.node(A, DISPATCH))
     # so the overlaps DBO is for are allowed
     assert not g.before(g.node(A, DISPATCH), g.node(B, ROUTE))
     assert not g.before(g.node(A, COMBINE), g.node(B, FFN))
     assert not g.before(g.node(B, DISPATCH), g.node(A, FFN)) and not g.before(g.node(A, FFN), g.node(B, DISPATCH))
 
 
-@pytest.mark.parametrize("shared", [False, True])
-def test_late_event_reproduces_over_serialisation(sched_bin, shared):
-    g = Graph(run_log(sched_bin, "late", shared)[0])
+def test_late_event_reproduces_over_serialisation(sched_bin):
+    g = Graph(run_log(sched_bin, "late")[0])
     A, B = 0, 1
     assert g.before(g.node(B, ROUTE), g.node(A, DISPATCH))
     assert g.before(g.node(B, FFN), g.node(A, COMBINE))
 
 
 def test_race_detector_catches_shared_workspace(sched_bin):
-    g = Graph(run_log(sched_bin, "dbo", True)[0])
+    g = Graph(run_log(sched_bin, "dbo")[0])
     found = races(g, halves=(0, 0))         # both microbatches on one workspace half
     assert found, "a shared workspace must show up as a race"
     assert any("ws0.ids" in c[4] or "ws0.w" in c[4] for c in found)
@@ -198,10 +190,10 @@ def test_race_detector_catches_shared_workspace(sched_bin):
 
 @pytest.mark.parametrize("schedule", ["dbo", "late", "serial"])
 def test_failure_injection(sched_bin, schedule):
-    full, _, _ = run_log(sched_bin, schedule, True)
+    full, _, _ = run_log(sched_bin, schedule)
     n_issued = sum(1 for o in full if o[0] in ("LAUNCH", "RECORD", "WAIT"))
     for fail_at in range(n_issued):
-        ops, status, _ = run_log(sched_bin, schedule, True, fail_at)
+        ops, status, _ = run_log(sched_bin, schedule, fail_at)
         assert status == -5
         issued = [o for o in ops if o[0] in ("LAUNCH", "RECORD", "WAIT")]
         assert len(issued) == fail_at                     # nothing after the failure
