@@ -7,24 +7,29 @@
 // activation dtype, y = h W2^T.
 #include <cmath>
 
-#include "gemm_mfma.h"
+#include "gemm_wstream.h"
 
 namespace dbomoe {
 
 // Rows per expert under roughly uniform routing are about Poisson(mean): size
-// the row tile for the likely largest expert so an expert's weights stream once
-// (weight-bound decode) and large experts get the big MFMA tile (prefill).
-static int choose_tile_m(int64_t mean_rows) {
+// the row tile for the likely largest expert.  Up to 32 rows the weights
+// dominate the bytes: the weight-streaming kernel (16-row tiles) where every K
+// fits its activation tile, else the 32-row LDS-tiled kernel; beyond that the
+// LDS-tiled kernel with 64- or 128-row tiles (prefill).
+static int choose_tile_m(int64_t mean_rows, bool ws_fits) {
   const double m = static_cast<double>(mean_rows);
   const double est_max = m + 3.0 * std::sqrt(m) + 1.0;
-  if (est_max <= 32) return 32;
+  if (est_max <= 32) return ws_fits ? 16 : 32;
   if (est_max <= 64) return 64;
   return 128;
 }
 
+// 16: weight-streaming kernel; 32/64/128: LDS-tiled kernel with that row tile.
 template <int MODE, bool FP8>
 static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g) {
-  if (bm == 32)
+  if (bm == 16)
+    hipLaunchKernelGGL((k_gemm_ws<MODE, FP8>), grid, dim3(kWsWaves * kWave), 0, s, g);
+  else if (bm == 32)
     hipLaunchKernelGGL((k_gemm_nt<32, 1, 4, MODE, FP8>), grid, dim3(256), 0, s, g);
   else if (bm == 64)
     hipLaunchKernelGGL((k_gemm_nt<64, 2, 2, MODE, FP8>), grid, dim3(256), 0, s, g);
@@ -111,12 +116,22 @@ static int64_t tiles_max(int bm, int64_t cap_rows, int E_loc, bool dense, int n_
   return rt0 * n_tiles0 + E1 * rt1 * n_tiles1;
 }
 
+// True if every GEMM of the call has K <= kWsKMax (the weight-streaming
+// kernel keeps the whole K of its activation tile in LDS).
+bool ffn_ws_fits(moe_dtype act, int32_t H, int32_t I, int64_t rows1, int32_t I1) {
+  if (act == MOE_F32 || H > kWsKMax || I > kWsKMax) return false;
+  if (rows1 > 0 && I1 / dense_down_chunks(act, I1, I) > kWsKMax) return false;
+  return true;
+}
+
 moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.cap_rows == 0 && a.rows1 == 0) return MOE_OK;
   if (a.act == MOE_F32) return launch_ffn_f32(a, s);
   const bool fp8 = a.wdt == MOE_FP8_E4M3FN;
   const bool dense = a.offsets == nullptr;
-  const int bm = a.tile_m > 0 ? a.tile_m : choose_tile_m(a.rows_hint);
+  const bool ws_fits = ffn_ws_fits(a.act, a.H, a.I, a.rows1, a.I1);
+  if (a.tile_m == 16 && !ws_fits) return MOE_ERR_UNSUPPORTED;
+  const int bm = a.tile_m > 0 ? a.tile_m : choose_tile_m(a.rows_hint, ws_fits);
 
   GemmParams p1{};
   p1.offsets = a.offsets;
@@ -211,7 +226,8 @@ extern "C" moe_status moe_grouped_ffn(const void* x_perm, moe_dtype act, int32_t
   if (st != MOE_OK) return st;
   if (cap_rows < 0) return MOE_ERR_INVALID_ARG;
   if (!offsets && E_loc != 1) return MOE_ERR_INVALID_ARG;
-  if (tile_m != 0 && tile_m != 32 && tile_m != 64 && tile_m != 128) return MOE_ERR_INVALID_ARG;
+  if (tile_m != 0 && tile_m != 16 && tile_m != 32 && tile_m != 64 && tile_m != 128) return MOE_ERR_INVALID_ARG;
+  if (tile_m == 16 && !ffn_ws_fits(act, H, I, 0, 0)) return MOE_ERR_UNSUPPORTED;
   if (cap_rows == 0) return MOE_OK;
   if (cap_rows > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (!x_perm || !w13 || !w2 || !y_perm || !ws) return MOE_ERR_INVALID_ARG;

@@ -16,9 +16,9 @@
 //    tiles run in the same launch instead of as a small grid of their own.
 //    Group 1 tiles come first in the tile order, so they start with the launch.
 //  * Workgroup b runs on XCD b % 8; the logical tile index is remapped so each
-//    XCD walks a contiguous run of tiles (column tiles of one row tile, then the
-//    next row tile of the same expert), keeping the A rows and the weight tile a
-//    neighbour needs in that XCD's L2.
+//    XCD walks a contiguous run of tiles.  Inside an expert the row tiles of one
+//    column tile come first, then the next column tile, so row tiles that share
+//    a weight tile run at the same time on one XCD and read it through its L2.
 //  * 4 waves; each wave owns a WM x WN block made of 16x16 MFMA tiles
 //    (v_mfma_f32_16x16x32_bf16, fp32 accumulators).  K advances 64 per stage.
 //    Global loads run two stages ahead of the MFMAs (a two-deep register ring)
@@ -125,23 +125,26 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int* s_loc, Til
         const int L1 = L % per_e;
         s_loc[1] = 1;
         s_loc[2] = L / per_e;
-        s_loc[3] = L1 / p.g[1].n_tiles;
-        s_loc[4] = L1 % p.g[1].n_tiles;
+        s_loc[3] = L1 % mt1;
+        s_loc[4] = L1 / mt1;
       }
     }
     if (valid && L >= tiles1) {
+      // Expert e owns tiles [nt0 * rt_before(e), nt0 * rt_through(e)), row
+      // tile fastest: the row tiles sharing a weight tile run back to back.
       const int L0 = L - tiles1;
-      const int mt = L0 / p.g[0].n_tiles;
+      const int nt0 = p.g[0].n_tiles;
       const int excl = incl - sum;
-      if (mt >= excl && mt < incl) {
+      if (L0 >= excl * nt0 && L0 < incl * nt0) {
         int acc = excl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (mt >= acc && mt < acc + t4[i]) {
+          if (L0 >= acc * nt0 && L0 < (acc + t4[i]) * nt0) {
+            const int local = L0 - acc * nt0;
             s_loc[1] = 0;
             s_loc[2] = lane * 4 + i;
-            s_loc[3] = mt - acc;
-            s_loc[4] = L0 % p.g[0].n_tiles;
+            s_loc[3] = local % t4[i];
+            s_loc[4] = local / t4[i];
           }
           acc += t4[i];
         }

@@ -140,7 +140,9 @@ moe_status moe_get_device_error(const void* dispatch_ws, int32_t* code, void* st
  *            per-128x128-block scales for fp8 (real W = code value * scale);
  *            must be NULL otherwise
  *   y_perm   [cap_rows, H] out, act; rows >= offsets[E_loc] untouched
- *   tile_m   0 = automatic; else 32, 64 or 128 rows per MFMA tile
+ *   tile_m   0 = automatic; 16 = the weight-streaming kernel (16-row tiles,
+ *            H and I <= 2048, else MOE_ERR_UNSUPPORTED); 32, 64 or 128 = the
+ *            LDS-tiled kernel with that many rows per tile
  *   ws       moe_ffn_workspace_size(cap_rows, I, act) bytes (holds h)
  * H % 128 == 0 and I % 64 == 0 (fp8: I % 128 == 0), else MOE_ERR_UNSUPPORTED.
  * fp8 weights are expanded to bf16 (code value x block scale, rounded once) on

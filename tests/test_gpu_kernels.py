@@ -173,7 +173,7 @@ def _ffn(C, x_perm, I, offsets, E_loc, w13, w2, s13=None, s2=None, tile_m=0):
 
 
 @pytest.mark.parametrize("cid", CIDS)
-@pytest.mark.parametrize("tile_m", [0, 32, 64, 128])
+@pytest.mark.parametrize("tile_m", [0, 16, 32, 64, 128])
 def test_grouped_ffn(cid, tile_m):
     C = _gpu()
     inp, ov = inputs(cid, True)
@@ -214,12 +214,41 @@ def test_ffn_single_row_experts_and_gaps():
     x = torch.randn(M, H).to(torch.bfloat16)
     w13 = (torch.randn(E, 2 * I, H) * 0.05).to(torch.bfloat16)
     w2 = (torch.randn(E, H, I) * 0.05).to(torch.bfloat16)
-    for tm in (32, 64, 128):
+    for tm in (16, 32, 64, 128):
         y = _ffn(C, x.cuda(), I, torch.from_numpy(offsets).cuda(), E, w13.cuda(), w2.cuda(), tile_m=tm)
         want, scale = O.grouped_ffn_ref(
             O.decode(W.bits(x), "bf16"), offsets,
             lambda e: (O.decode(W.bits(w13[e]), "bf16"), O.decode(W.bits(w2[e]), "bf16")), with_scale=True)
         assert_close(to_f64(y), want, 1e-2, f"ragged experts tile_m={tm}", scale)
+
+
+@pytest.mark.parametrize("cid", [2, 5])
+def test_weight_streaming_kernel_matches_lds_kernel_bitwise(cid):
+    """bf16: the weight-streaming kernel (16-row tiles) and the LDS-tiled kernel
+    (32-row tiles) run the same MFMA over the same K order, so their outputs
+    agree bit for bit; K = 192 and 1408-like lengths exercise the partial chunk."""
+    C = _gpu()
+    inp, ov = inputs(cid, True)
+    cfg = inp["cfg"]
+    ids = O.moe_layer_expert(ov, tokens=np.arange(1))["ids"]
+    ref = O.dispatch_ref(ids, cfg.expert_begin, cfg.expert_end)
+    x_perm = inp["x"][torch.from_numpy(ref["perm"] // cfg.k).long()].contiguous().cuda()
+    off = torch.from_numpy(ref["offsets"]).cuda()
+    ys = [_ffn(C, x_perm, cfg.I, off, cfg.E_loc, inp["w13"].cuda(), inp["w2"].cuda(), tile_m=tm)[:ref["M"]]
+          for tm in (16, 32)]
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+    # a long K with a partial chunk: H = 2048 (8 full chunks), I = 1408 (4 + 5 x 8 steps)
+    rng = torch.Generator().manual_seed(11)
+    H, I, E = 2048, 1408, 3
+    counts = np.array([5, 0, 21])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offsets[-1])
+    x = torch.randn(M, H, generator=rng).to(torch.bfloat16).cuda()
+    w13 = (torch.randn(E, 2 * I, H, generator=rng) * 0.02).to(torch.bfloat16).cuda()
+    w2 = (torch.randn(E, H, I, generator=rng) * 0.02).to(torch.bfloat16).cuda()
+    off = torch.from_numpy(offsets).cuda()
+    ys = [_ffn(C, x, I, off, E, w13, w2, tile_m=tm) for tm in (16, 32)]
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
 
 
 @pytest.mark.parametrize("cid", CIDS)
