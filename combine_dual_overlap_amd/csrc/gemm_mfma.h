@@ -351,22 +351,46 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
 
   // Two-deep register ring: stage s is loaded into ring slot s % 2 two stages
   // before its MFMAs and stored to LDS buffer s % 2 one stage before them.
+  // The steady-state loop issues its loads unconditionally (the last stages
+  // are peeled), and scheduling barriers keep them ahead of the MFMAs: with a
+  // conditional or sunk load the compiler's wait for one stage also waits for
+  // the stage issued after it, and the ring degenerates to one stage.
   load_stage(0, ra0, rb0, sc0);
   if (KT > 1) load_stage(1, ra1, rb1, sc1);
   store_stage(0, ra0, rb0, sc0);
   __syncthreads();
   int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    if (kt + 2 < KT) load_stage(kt + 2, ra0, rb0, sc0);
+  for (; kt + 3 < KT; kt += 2) {
+    load_stage(kt + 2, ra0, rb0, sc0);
+    __builtin_amdgcn_sched_barrier(0);
     compute_stage(0);
     store_stage(1, ra1, rb1, sc1);
     __syncthreads();
-    if (kt + 3 < KT) load_stage(kt + 3, ra1, rb1, sc1);
+    load_stage(kt + 3, ra1, rb1, sc1);
+    __builtin_amdgcn_sched_barrier(0);
     compute_stage(1);
-    if (kt + 2 < KT) store_stage(0, ra0, rb0, sc0);
+    store_stage(0, ra0, rb0, sc0);
     __syncthreads();
   }
-  if (kt < KT) compute_stage(0);
+  const int left = KT - kt;                 // 1, 2 or 3 stages; stage kt is in LDS buffer 0
+  if (left == 3) {
+    load_stage(kt + 2, ra0, rb0, sc0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage(0);
+    store_stage(1, ra1, rb1, sc1);
+    __syncthreads();
+    compute_stage(1);
+    store_stage(0, ra0, rb0, sc0);
+    __syncthreads();
+    compute_stage(0);
+  } else if (left == 2) {
+    compute_stage(0);
+    store_stage(1, ra1, rb1, sc1);
+    __syncthreads();
+    compute_stage(1);
+  } else {
+    compute_stage(0);
+  }
 
   // Epilogue.  Accumulator element r of lane l in a 16x16 tile is
   // (row 4*(l/16) + r, column l%16).
