@@ -24,7 +24,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
-KERNEL_SOURCES = ["combine_dual_overlap_amd/csrc/gemm_mfma.h", "combine_dual_overlap_amd/csrc/ffn.hip"]
+KERNEL_SOURCES = ["combine_dual_overlap_amd/csrc/gemm_mfma.h", "combine_dual_overlap_amd/csrc/gemm_wstream.h",
+                  "combine_dual_overlap_amd/csrc/ffn.hip"]
 
 
 def log(*a):
@@ -131,6 +132,7 @@ def main():
     import torch
     import workloads as W
     from combine_dual_overlap_amd import DeviceLayer
+    from combine_dual_overlap_amd import binding as B
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate_copy_mib > 0:
@@ -201,7 +203,13 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                 "frac": round(achieved / mfma_peak, 4)}
     roof["traffic"] = traffic
-    roof["kernel"] = "gate/up expert GEMM + SwiGLU, routed and shared experts (k_gemm_nt MODE_GATEUP)"
+    T_mb0 = halves[0][1] - halves[0][0]
+    I_sh = cfg.n_shared * cfg.shared_I
+    tile = B.moe_ffn_auto_tile(B.dtype_code(L.x), B.dtype_code(L.w13), cfg.H, cfg.I, -(-T_mb0 * cfg.k // cfg.E),
+                               T_mb0 if I_sh else 0, I_sh)
+    kname = ("k_gemm_nt_f32 (fp32 SIMT)" if cfg.act == "f32" else
+             "k_gemm_ws (weight-streaming, 16-row tiles)" if tile == 16 else f"k_gemm_nt ({tile}-row LDS tiles)")
+    roof["kernel"] = f"gate/up expert GEMM + SwiGLU, routed and shared experts: {kname}, MODE_GATEUP"
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
     roof["algorithmic_bytes_per_launch"] = int(bytes_launch)
     roof["algorithmic_flops_per_launch"] = int(flops_launch)

@@ -24,7 +24,7 @@ SCHEDULES = {"unsplit": 0, "serial": 1, "dbo": 2, "dbo_late_event": 3}
 
 EXPORTED = [
     "moe_route_workspace_size", "moe_route_topk", "moe_dispatch_workspace_size", "moe_dispatch",
-    "moe_get_device_error", "moe_ffn_workspace_size", "moe_grouped_ffn", "moe_combine",
+    "moe_get_device_error", "moe_ffn_workspace_size", "moe_ffn_auto_tile", "moe_grouped_ffn", "moe_combine",
     "dbo_ctx_create", "dbo_ctx_destroy", "dbo_ctx_set_timing", "dbo_ctx_ffn_times", "dbo_ctx_last_stats",
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "dbo_moe_layer", "moe_status_string",
 ]
@@ -80,6 +80,7 @@ def lib():
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
             "moe_get_device_error": (_i32, [_vp, ctypes.POINTER(_i32), _vp]),
             "moe_ffn_workspace_size": (_sz, [_i64, _i32, _i32]),
+            "moe_ffn_auto_tile": (_i32, [_i32, _i32, _i32, _i32, _i64, _i64, _i32]),
             "moe_grouped_ffn": (_i32, [_vp, _i32, _i32, _i32, _vp, _i32, _i64, _vp, _vp, _i32, _vp, _vp,
                                        _vp, _i32, _vp, _sz, _vp]),
             "moe_combine": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -182,6 +183,11 @@ def moe_get_device_error(dispatch_ws, stream=None) -> int:
 
 def moe_ffn_workspace_size(cap_rows: int, I: int, act: int) -> int:
     return lib().moe_ffn_workspace_size(cap_rows, I, act)
+
+
+def moe_ffn_auto_tile(act: int, wdt: int, H: int, I: int, rows_per_expert: int, rows1: int = 0,
+                      I1: int = 0) -> int:
+    return lib().moe_ffn_auto_tile(act, wdt, H, I, rows_per_expert, rows1, I1)
 
 
 def moe_grouped_ffn(x_perm, I, offsets, E_loc, w13, w2, y_perm, ws, w13_scale=None, w2_scale=None,

@@ -211,6 +211,16 @@ size_t ffn_ws_bytes(int64_t cap_rows, int32_t I, moe_dtype act) {
 
 using namespace dbomoe;
 
+extern "C" int32_t moe_ffn_auto_tile(moe_dtype act, moe_dtype wdt, int32_t H, int32_t I, int64_t rows_per_expert,
+                                     int64_t rows1, int32_t I1) {
+  if (check_ffn_shapes(act, wdt, H, I, 1, wdt == MOE_FP8_E4M3FN ? reinterpret_cast<const float*>(16) : nullptr,
+                       wdt == MOE_FP8_E4M3FN ? reinterpret_cast<const float*>(16) : nullptr) != MOE_OK ||
+      rows_per_expert < 0 || rows1 < 0 || (rows1 > 0 && I1 <= 0))
+    return 0;
+  if (act == MOE_F32) return 32;
+  return choose_tile_m(rows_per_expert, ffn_ws_fits(act, H, I, rows1, I1));
+}
+
 extern "C" size_t moe_ffn_workspace_size(int64_t cap_rows, int32_t I, moe_dtype act) {
   if (cap_rows < 0 || I <= 0 || (act != MOE_F32 && act != MOE_BF16)) return 0;
   return ffn_ws_bytes(cap_rows, I, act);

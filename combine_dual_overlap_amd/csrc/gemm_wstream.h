@@ -62,95 +62,75 @@ __device__ __forceinline__ int ws_koff(int s, int g) {
   return 32 * s + 8 * g;
 }
 
-// Column tiles of the weight-streaming kernel for a GEMM with N outputs.
-inline int ws_col_tiles(int mode, int N) {
-  return mode == MODE_GATEUP ? (N + kWsBN / 2 - 1) / (kWsBN / 2) : (N + kWsBN - 1) / kWsBN;
-}
-
 // One K chunk of NS steps from a wave's two weight subtiles: NS 16-byte loads
 // per subtile for bf16, NS/2 for fp8 (each holds two steps).
 template <int NS, bool FP8>
 struct WsChunk {
   static constexpr int LOADS = FP8 ? NS / 2 : NS;
+  static constexpr int STEPS = NS;
   u32x4_t b[2][LOADS];
 };
 
-// The tile: KS steps per full chunk, REM steps in a last, partial chunk (0 if
-// K is a multiple of the chunk).  Every load and MFMA inside a chunk is
-// unconditional, so the compiler can keep all of a chunk's loads in flight.
-template <int KS, int REM, int MODE, bool FP8>
-__device__ __forceinline__ void gemm_tile_ws(const GemmGroup& g, const TileLoc& t, bf16_t* sA) {
-  constexpr int TM = kWsRows / 16;              // activation subtiles
-  constexpr int KC = KS * 32;                   // K per full chunk
-  static_assert(!FP8 || (KS % 2 == 0 && REM % 2 == 0), "fp8 steps come in pairs");
-  using Full = WsChunk<KS, FP8>;
-  using Part = WsChunk<(REM > 0 ? REM : 2), FP8>;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int frow = lane & 15;
-  const int fg = lane >> 4;
-  const int K = g.K;
-  const int lrow = (K + 127) & ~127;            // LDS row length: whole swizzle runs
-  const int nt = t.nt;
-
-  // ---- this wave's two 16-row weight subtiles
-  int wrow[2];
-  bool live;
-  if constexpr (MODE == MODE_GATEUP) {
-    const int col0 = nt * (kWsBN / 2) + wave * 16;          // first output column of the wave
-    live = col0 < g.N;
-    wrow[0] = col0 + frow;                                  // gate
-    wrow[1] = g.N + col0 + frow;                            // matching up
-  } else {
-    const int r0 = nt * kWsBN + wave * 32;
-    live = r0 < g.N;
-    wrow[0] = r0 + frow;
-    wrow[1] = r0 + 16 + frow;
-  }
+// One wave's share of a column tile: 32 weight rows (gate/up: 16 gate rows and
+// the 16 matching up rows; down: 32 consecutive rows) against TM 16-row
+// activation subtiles held in LDS.  The host keeps every wave's rows inside
+// the matrix (I % 64 == 0 for 64 gate/up columns per tile, H % 128 == 0).
+template <int TM, int MODE, bool FP8>
+struct WsWave {
   const uint8_t* bptr[2];
+  const float* srow[2];
+  int wrow[2];
+  int frow, fg;
+  f32x4_t acc[TM][2];
+
+  __device__ __forceinline__ void init(const GemmGroup& g, const TileLoc& t) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    frow = lane & 15;
+    fg = lane >> 4;
+    if constexpr (MODE == MODE_GATEUP) {
+      wrow[0] = t.nt * (kWsBN / 2) + wave * 16 + frow;     // gate
+      wrow[1] = g.N + wrow[0];                              // matching up
+    } else {
+      wrow[0] = t.nt * kWsBN + wave * 32 + frow;
+      wrow[1] = wrow[0] + 16;
+    }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const size_t row_elem = static_cast<size_t>(t.e) * g.b_estride + static_cast<size_t>(wrow[j]) * g.ldb;
-    bptr[j] = FP8 ? static_cast<const uint8_t*>(g.B) + row_elem + 16 * fg
-                  : reinterpret_cast<const uint8_t*>(static_cast<const bf16_t*>(g.B) + row_elem + 8 * fg);
-  }
-  const float* srow[2] = {nullptr, nullptr};
-  if constexpr (FP8) {
-    const int kblocks = K / 128;
-    const float* se = g.bscale + static_cast<size_t>(t.e) * (g.b_rows / 128) * kblocks;
+    for (int j = 0; j < 2; ++j) {
+      const size_t row_elem = static_cast<size_t>(t.e) * g.b_estride + static_cast<size_t>(wrow[j]) * g.ldb;
+      bptr[j] = FP8 ? static_cast<const uint8_t*>(g.B) + row_elem + 16 * fg
+                    : reinterpret_cast<const uint8_t*>(static_cast<const bf16_t*>(g.B) + row_elem + 8 * fg);
+      srow[j] = nullptr;
+    }
+    if constexpr (FP8) {
+      const int kblocks = g.K / 128;
+      const float* se = g.bscale + static_cast<size_t>(t.e) * (g.b_rows / 128) * kblocks;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) srow[j] = se + static_cast<size_t>((wrow[j] - frow) / 128) * kblocks;
+      for (int j = 0; j < 2; ++j) srow[j] = se + static_cast<size_t>((wrow[j] - frow) / 128) * kblocks;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // K is cut into a partial chunk of REM steps first (if any), then full
-  // chunks of KS steps.
-  const int kp = REM * 32;                      // K where the full chunks start
-  const int n_full = (K - kp) / KC;
-
-  // 16-byte load l of subtile j in the chunk starting at K offset k0
-  auto load = [&](auto& ch, int k0) {
-    constexpr int L = std::remove_reference_t<decltype(ch)>::LOADS;
+  // The chunk of weights starting at K offset k0.
+  template <class Ch>
+  __device__ __forceinline__ void load(Ch& ch, int k0) const {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int l = 0; l < L; ++l) {
+      for (int l = 0; l < Ch::LOADS; ++l) {
         const size_t off = FP8 ? static_cast<size_t>(k0) + 64 * l : (static_cast<size_t>(k0) + 32 * l) * 2;
         ch.b[j][l] = *reinterpret_cast<const u32x4_t*>(bptr[j] + off);
       }
-  };
+  }
 
-  f32x4_t acc[TM][2];
+  // MFMAs of the chunk at K offset k0; its activations sit in LDS columns
+  // starting at k0 - kbase of rows `lrow` elements long.
+  template <class Ch>
+  __device__ __forceinline__ void compute(const Ch& ch, int k0, const bf16_t* sA, int lrow, int kbase) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const auto& ch, int k0) {
-    constexpr int NS = FP8 ? 2 * std::remove_reference_t<decltype(ch)>::LOADS
-                           : std::remove_reference_t<decltype(ch)>::LOADS;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int kc = (k0 + ws_koff<FP8>(s, fg)) >> 3;
+    for (int s = 0; s < Ch::STEPS; ++s) {
+      const int kc = (k0 - kbase + ws_koff<FP8>(s, fg)) >> 3;
       bf16x8_t af[TM];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
@@ -178,19 +158,58 @@ __device__ __forceinline__ void gemm_tile_ws(const GemmGroup& g, const TileLoc& 
           acc[tm][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bv, acc[tm][j], 0, 0, 0);
       }
     }
-  };
+  }
 
+  // Accumulator element r of lane l is (row 4*(l/16) + r, column l%16).
+  __device__ __forceinline__ void store(const GemmGroup& g, const TileLoc& t) const {
+    const int row_q = fg * 4;
+    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mr = t.m_off + tm * 16 + row_q + r;
+        if (mr >= t.rows) continue;
+        bf16_t* Cr = C + (t.row_begin + mr) * g.ldc;
+        if constexpr (MODE == MODE_GATEUP) {
+          Cr[wrow[0]] = f32_to_bf16(silu_f32(acc[tm][0][r]) * acc[tm][1][r]);
+        } else {
+          Cr[wrow[0]] = f32_to_bf16(acc[tm][0][r]);
+          Cr[wrow[1]] = f32_to_bf16(acc[tm][1][r]);
+        }
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Whole-K activation tile (K <= 2048), 16-row tiles.
+// KS steps per full chunk, REM steps in a first, partial chunk (0 if K is a
+// multiple of the chunk).  Every load and MFMA inside a chunk is
+// unconditional, so the compiler can keep all of a chunk's loads in flight.
+template <int KS, int REM, int MODE, bool FP8>
+__device__ __forceinline__ void gemm_tile_ws(const GemmGroup& g, const TileLoc& t, bf16_t* sA) {
+  constexpr int KC = KS * 32;                   // K per full chunk
+  static_assert(!FP8 || (KS % 2 == 0 && REM % 2 == 0), "fp8 steps come in pairs");
+  using Full = WsChunk<KS, FP8>;
+  using Part = WsChunk<(REM > 0 ? REM : 2), FP8>;
+
+  const int tid = threadIdx.x;
+  const int K = g.K;
+  const int lrow = (K + 127) & ~127;            // LDS row length: whole swizzle runs
+  WsWave<kWsRows / 16, MODE, FP8> w;
+  w.init(g, t);
+
+  const int kp = REM * 32;                      // K where the full chunks start
+  const int n_full = (K - kp) / KC;
+  auto kfull = [&](int c) { return kp + c * KC; };
   Full b0, b1;
   Part bp;
-  auto kfull = [&](int c) { return kp + c * KC; };
 
-  // ---- weights of the partial chunk and the first full chunk are issued
-  // ahead of the activation tile, the second full chunk behind it.  Rows past
-  // the tile's end read the tile's last row (never stored out).
-  if (live) {
-    if constexpr (REM > 0) load(bp, 0);
-    if (n_full > 0) load(b0, kfull(0));
-  }
+  // Weights of the partial chunk and the first full chunk are issued ahead of
+  // the activation tile, the second full chunk behind it.  Rows past the
+  // tile's end read the tile's last row (never stored out).
+  if constexpr (REM > 0) w.load(bp, 0);
+  if (n_full > 0) w.load(b0, kfull(0));
   {
     constexpr int kThreads = kWsWaves * kWave;
     constexpr int kPer = kWsRows * kWsKMax / 8 / kThreads;   // 16-byte chunks per thread at K = kWsKMax
@@ -213,65 +232,41 @@ __device__ __forceinline__ void gemm_tile_ws(const GemmGroup& g, const TileLoc& 
       if (c < total) *reinterpret_cast<u32x4_t*>(&sA[ws_lds(c / chunks, c % chunks, lrow)]) = v[i];
     }
   }
-  if (live && n_full > 1) load(b1, kfull(1));
-  __syncthreads();                                          // activation tile complete
-  if (!live) return;                                        // no barrier follows
+  if (n_full > 1) w.load(b1, kfull(1));
+  __syncthreads();                                          // activation tile complete; no barrier follows
 
-  if constexpr (REM > 0) compute(bp, 0);
+  if constexpr (REM > 0) w.compute(bp, 0, sA, lrow, 0);
   // Steady state: both next chunks exist, so both loads are unconditional and
-  // chunk c + 1 stays in flight while chunk c is multiplied.
+  // chunk c + 1 stays in flight while chunk c is multiplied.  The scheduling
+  // barriers keep each chunk's loads where they are issued: the compiler would
+  // otherwise sink them below the next chunk's MFMAs, and the wait for one
+  // chunk would then also wait for the other.
   int c = 0;
-  // The scheduling barriers keep each chunk's loads where they are issued: the
-  // compiler would otherwise sink them below the next chunk's MFMAs, and the
-  // wait for one chunk would then also wait for the other.
   for (; c + 3 < n_full; c += 2) {
-    compute(b0, kfull(c));
+    w.compute(b0, kfull(c), sA, lrow, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load(b0, kfull(c + 2));
+    w.load(b0, kfull(c + 2));
     __builtin_amdgcn_sched_barrier(0);
-    compute(b1, kfull(c + 1));
+    w.compute(b1, kfull(c + 1), sA, lrow, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load(b1, kfull(c + 3));
+    w.load(b1, kfull(c + 3));
     __builtin_amdgcn_sched_barrier(0);
   }
   const int left = n_full - c;                              // 0..3
   if (left == 3) {
-    compute(b0, kfull(c));
+    w.compute(b0, kfull(c), sA, lrow, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load(b0, kfull(c + 2));
+    w.load(b0, kfull(c + 2));
     __builtin_amdgcn_sched_barrier(0);
-    compute(b1, kfull(c + 1));
-    compute(b0, kfull(c + 2));
+    w.compute(b1, kfull(c + 1), sA, lrow, 0);
+    w.compute(b0, kfull(c + 2), sA, lrow, 0);
   } else if (left == 2) {
-    compute(b0, kfull(c));
-    compute(b1, kfull(c + 1));
+    w.compute(b0, kfull(c), sA, lrow, 0);
+    w.compute(b1, kfull(c + 1), sA, lrow, 0);
   } else if (left == 1) {
-    compute(b0, kfull(c));
+    w.compute(b0, kfull(c), sA, lrow, 0);
   }
-
-  // ---- epilogue: accumulator element r of lane l is (row 4*(l/16) + r, column l%16)
-  const int row_q = fg * 4;
-  bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
-  if constexpr (MODE == MODE_GATEUP) {
-    const int col = wrow[0];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int mr = t.m_off + tm * 16 + row_q + r;
-        if (mr < t.rows) C[(t.row_begin + mr) * g.ldc + col] = f32_to_bf16(silu_f32(acc[tm][0][r]) * acc[tm][1][r]);
-      }
-  } else {
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int mr = t.m_off + tm * 16 + row_q + r;
-          if (mr < t.rows) C[(t.row_begin + mr) * g.ldc + wrow[j]] = f32_to_bf16(acc[tm][j][r]);
-        }
-  }
+  w.store(g, t);
 }
 
 // Dispatches on the partial chunk's step count (bf16 K is a multiple of 64,
@@ -305,6 +300,130 @@ __global__ __launch_bounds__(kWsWaves * kWave, 2) void k_gemm_ws(GemmParams p) {
     gemm_tile_ws_rem<16, MODE, FP8>(p.g[0], t, sA);
   else
     gemm_tile_ws_rem<8, MODE, false>(p.g[t.grp], t, sA);
+}
+
+// ---------------------------------------------------------------------------
+// Phased activation tile (any K that is a multiple of the chunk), BM-row tiles.
+// The activation tile moves through LDS one chunk of K at a time, double
+// buffered: while chunk p is multiplied, chunk p + 1 is loaded into registers
+// and stored into the other buffer, and one barrier per chunk hands the
+// buffers over.  The weights stream exactly as in the whole-K kernel.
+template <int BM, int KS, int MODE, bool FP8>
+__device__ __forceinline__ void gemm_tile_wsp(const GemmGroup& g, const TileLoc& t, bf16_t* sA) {
+  constexpr int TM = BM / 16;
+  constexpr int KC = KS * 32;                   // K per chunk (a multiple of 128)
+  constexpr int CPR = KC / 8;                   // 16-byte activation chunks per row per chunk
+  constexpr int CA = BM * CPR / (kWsWaves * kWave);
+  static_assert(KC % 128 == 0 && CA >= 1 && BM * CPR % (kWsWaves * kWave) == 0, "phase shape");
+  using Full = WsChunk<KS, FP8>;
+
+  const int tid = threadIdx.x;
+  const int n = g.K / KC;                       // chunks (the host checks K % KC == 0)
+  WsWave<TM, MODE, FP8> w;
+  w.init(g, t);
+
+  // Thread tid moves 16-byte chunk (tid % CPR) of tile rows tid / CPR + i * RSTEP.
+  constexpr int RSTEP = kWsWaves * kWave / CPR;
+  static_assert(kWsWaves * kWave % CPR == 0, "a thread keeps one column of the chunk");
+  const int a_kc = tid % CPR;
+  const int a_r0 = tid / CPR;
+  const bf16_t* a_base = g.A + t.e * g.a_estride + t.row_begin * g.lda + a_kc * 8;
+  u32x4_t ra[CA];
+  auto load_a = [&](int p) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      int mr = t.m_off + a_r0 + i * RSTEP;
+      mr = mr < t.rows ? mr : t.rows - 1;       // rows past the tile's end read its last row
+      ra[i] = *reinterpret_cast<const u32x4_t*>(a_base + mr * g.lda + static_cast<int64_t>(p) * KC);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i)
+      *reinterpret_cast<u32x4_t*>(&sA[buf * BM * KC + ws_lds(a_r0 + i * RSTEP, a_kc, KC)]) = ra[i];
+  };
+  auto compute = [&](const Full& b, int p) { w.compute(b, p * KC, sA + (p & 1) * BM * KC, KC, p * KC); };
+
+  Full b0, b1;
+  w.load(b0, 0);
+  load_a(0);
+  store_a(0);
+  if (n > 1) w.load(b1, KC);
+  __syncthreads();
+
+  // Steady state (chunks p + 2 and p + 3 exist): every load unconditional.
+  int p = 0;
+  for (; p + 3 < n; p += 2) {
+    load_a(p + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b0, p);
+    __builtin_amdgcn_sched_barrier(0);
+    w.load(b0, (p + 2) * KC);
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(1);
+    __syncthreads();
+    load_a(p + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1, p + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    w.load(b1, (p + 3) * KC);
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(0);
+    __syncthreads();
+  }
+  const int left = n - p;                       // 1..3; chunk p is in buffer 0
+  if (left == 3) {
+    load_a(p + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b0, p);
+    __builtin_amdgcn_sched_barrier(0);
+    w.load(b0, (p + 2) * KC);
+    __builtin_amdgcn_sched_barrier(0);
+    store_a(1);
+    __syncthreads();
+    load_a(p + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1, p + 1);
+    store_a(0);
+    __syncthreads();
+    compute(b0, p + 2);
+  } else if (left == 2) {
+    load_a(p + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b0, p);
+    store_a(1);
+    __syncthreads();
+    compute(b1, p + 1);
+  } else {
+    compute(b0, p);
+  }
+  w.store(g, t);
+}
+
+// Chunk lengths of the phased kernel: 512 bytes of each weight row for
+// 32-row tiles (fp8 KS 16, bf16 KS 8), 256 bytes for 64-row tiles (fp8 KS 8,
+// bf16 KS 4), so the double-buffered activation chunk stays at 64 KB of LDS.
+template <int BM, bool FP8, int KS_FP8 = 0>
+struct WspShape {
+  static constexpr int KS = !FP8 ? (BM == 32 ? 8 : 4) : KS_FP8 > 0 ? KS_FP8 : (BM == 32 ? 16 : 8);
+  static constexpr int KS_BF16 = BM == 32 ? 8 : 4;         // dense group of an fp8 launch
+  static constexpr int KC = KS * 32;
+  static constexpr int KC_BF16 = KS_BF16 * 32;
+};
+
+template <int BM, int MODE, bool FP8, int KS_FP8 = 0>
+__global__ __launch_bounds__(kWsWaves * kWave, 2) void k_gemm_wsp(GemmParams p) {
+  using S = WspShape<BM, FP8, KS_FP8>;
+  constexpr int kLds = 2 * BM * (S::KC > S::KC_BF16 ? S::KC : S::KC_BF16);
+  __shared__ __attribute__((aligned(16))) bf16_t sA[kLds];
+  int* s_loc = reinterpret_cast<int*>(&sA[0]);
+  TileLoc t;
+  if (!locate_tile<BM>(p, s_loc, t)) return;
+  __syncthreads();                                  // s_loc read by all before sA is filled
+  if (FP8 && t.grp == 0)
+    gemm_tile_wsp<BM, S::KS, MODE, FP8>(p.g[0], t, sA);
+  else
+    gemm_tile_wsp<BM, S::KS_BF16, MODE, false>(p.g[t.grp], t, sA);
 }
 
 }  // namespace dbomoe

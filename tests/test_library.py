@@ -70,6 +70,20 @@ def test_layer_workspace_size_and_validation():
     assert lay["logits"] == n // 2 and all(v % 256 == 0 for v in lay.values())
 
 
+def test_ffn_auto_tile_choice():
+    from combine_dual_overlap_amd import binding as B
+    # decode-sized experts with H, I <= 2048: the weight-streaming kernel
+    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_BF16, 2048, 1408, 12, 128, 2816) == 16
+    # the same rows with H = 7168: the activation tile no longer fits LDS
+    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 7168, 2048, 12) == 32
+    # prefill-sized experts
+    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 2048, 768, 256) == 128
+    assert B.moe_ffn_auto_tile(B.MOE_F32, B.MOE_F32, 128, 256, 8) == 32
+    # invalid shapes
+    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_BF16, 2048, 1400, 12) == 0
+    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 2048, 192, 12) == 0
+
+
 def test_entry_points_reject_bad_arguments_without_a_device():
     from combine_dual_overlap_amd import binding as B
     L = B.lib()
