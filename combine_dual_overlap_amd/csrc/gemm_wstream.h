@@ -302,128 +302,4 @@ __global__ __launch_bounds__(kWsWaves * kWave, 2) void k_gemm_ws(GemmParams p) {
     gemm_tile_ws_rem<8, MODE, false>(p.g[t.grp], t, sA);
 }
 
-// ---------------------------------------------------------------------------
-// Phased activation tile (any K that is a multiple of the chunk), BM-row tiles.
-// The activation tile moves through LDS one chunk of K at a time, double
-// buffered: while chunk p is multiplied, chunk p + 1 is loaded into registers
-// and stored into the other buffer, and one barrier per chunk hands the
-// buffers over.  The weights stream exactly as in the whole-K kernel.
-template <int BM, int KS, int MODE, bool FP8>
-__device__ __forceinline__ void gemm_tile_wsp(const GemmGroup& g, const TileLoc& t, bf16_t* sA) {
-  constexpr int TM = BM / 16;
-  constexpr int KC = KS * 32;                   // K per chunk (a multiple of 128)
-  constexpr int CPR = KC / 8;                   // 16-byte activation chunks per row per chunk
-  constexpr int CA = BM * CPR / (kWsWaves * kWave);
-  static_assert(KC % 128 == 0 && CA >= 1 && BM * CPR % (kWsWaves * kWave) == 0, "phase shape");
-  using Full = WsChunk<KS, FP8>;
-
-  const int tid = threadIdx.x;
-  const int n = g.K / KC;                       // chunks (the host checks K % KC == 0)
-  WsWave<TM, MODE, FP8> w;
-  w.init(g, t);
-
-  // Thread tid moves 16-byte chunk (tid % CPR) of tile rows tid / CPR + i * RSTEP.
-  constexpr int RSTEP = kWsWaves * kWave / CPR;
-  static_assert(kWsWaves * kWave % CPR == 0, "a thread keeps one column of the chunk");
-  const int a_kc = tid % CPR;
-  const int a_r0 = tid / CPR;
-  const bf16_t* a_base = g.A + t.e * g.a_estride + t.row_begin * g.lda + a_kc * 8;
-  u32x4_t ra[CA];
-  auto load_a = [&](int p) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      int mr = t.m_off + a_r0 + i * RSTEP;
-      mr = mr < t.rows ? mr : t.rows - 1;       // rows past the tile's end read its last row
-      ra[i] = *reinterpret_cast<const u32x4_t*>(a_base + mr * g.lda + static_cast<int64_t>(p) * KC);
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i)
-      *reinterpret_cast<u32x4_t*>(&sA[buf * BM * KC + ws_lds(a_r0 + i * RSTEP, a_kc, KC)]) = ra[i];
-  };
-  auto compute = [&](const Full& b, int p) { w.compute(b, p * KC, sA + (p & 1) * BM * KC, KC, p * KC); };
-
-  Full b0, b1;
-  w.load(b0, 0);
-  load_a(0);
-  store_a(0);
-  if (n > 1) w.load(b1, KC);
-  __syncthreads();
-
-  // Steady state (chunks p + 2 and p + 3 exist): every load unconditional.
-  int p = 0;
-  for (; p + 3 < n; p += 2) {
-    load_a(p + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b0, p);
-    __builtin_amdgcn_sched_barrier(0);
-    w.load(b0, (p + 2) * KC);
-    __builtin_amdgcn_sched_barrier(0);
-    store_a(1);
-    __syncthreads();
-    load_a(p + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b1, p + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    w.load(b1, (p + 3) * KC);
-    __builtin_amdgcn_sched_barrier(0);
-    store_a(0);
-    __syncthreads();
-  }
-  const int left = n - p;                       // 1..3; chunk p is in buffer 0
-  if (left == 3) {
-    load_a(p + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b0, p);
-    __builtin_amdgcn_sched_barrier(0);
-    w.load(b0, (p + 2) * KC);
-    __builtin_amdgcn_sched_barrier(0);
-    store_a(1);
-    __syncthreads();
-    load_a(p + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b1, p + 1);
-    store_a(0);
-    __syncthreads();
-    compute(b0, p + 2);
-  } else if (left == 2) {
-    load_a(p + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b0, p);
-    store_a(1);
-    __syncthreads();
-    compute(b1, p + 1);
-  } else {
-    compute(b0, p);
-  }
-  w.store(g, t);
-}
-
-// Chunk lengths of the phased kernel: 512 bytes of each weight row for
-// 32-row tiles (fp8 KS 16, bf16 KS 8), 256 bytes for 64-row tiles (fp8 KS 8,
-// bf16 KS 4), so the double-buffered activation chunk stays at 64 KB of LDS.
-template <int BM, bool FP8, int KS_FP8 = 0>
-struct WspShape {
-  static constexpr int KS = !FP8 ? (BM == 32 ? 8 : 4) : KS_FP8 > 0 ? KS_FP8 : (BM == 32 ? 16 : 8);
-  static constexpr int KS_BF16 = BM == 32 ? 8 : 4;         // dense group of an fp8 launch
-  static constexpr int KC = KS * 32;
-  static constexpr int KC_BF16 = KS_BF16 * 32;
-};
-
-template <int BM, int MODE, bool FP8, int KS_FP8 = 0>
-__global__ __launch_bounds__(kWsWaves * kWave, 2) void k_gemm_wsp(GemmParams p) {
-  using S = WspShape<BM, FP8, KS_FP8>;
-  constexpr int kLds = 2 * BM * (S::KC > S::KC_BF16 ? S::KC : S::KC_BF16);
-  __shared__ __attribute__((aligned(16))) bf16_t sA[kLds];
-  int* s_loc = reinterpret_cast<int*>(&sA[0]);
-  TileLoc t;
-  if (!locate_tile<BM>(p, s_loc, t)) return;
-  __syncthreads();                                  // s_loc read by all before sA is filled
-  if (FP8 && t.grp == 0)
-    gemm_tile_wsp<BM, S::KS, MODE, FP8>(p.g[0], t, sA);
-  else
-    gemm_tile_wsp<BM, S::KS_BF16, MODE, false>(p.g[t.grp], t, sA);
-}
-
 }  // namespace dbomoe
