@@ -4,9 +4,7 @@
 // Dual-Batch Overlap mechanism to VLLM", Purpose:
 //   out[t] = sum_j [inv[t*k+j] >= 0] w[t, j] * y_perm[inv[t*k+j]]  (+ shared[t])
 // summed in j order in fp32 and rounded once.  HBM-bound: every dispatched row
-// is read once and every token row written once.  One wave per token; the k
-// source rows of a chunk are all loaded before any is accumulated, so a wave has
-// up to KMAX x CH 16-byte loads in flight.
+// is read once and every token row written once.
 #include "common.h"
 
 namespace dbomoe {
@@ -36,88 +34,108 @@ __device__ __forceinline__ u32x4_t pack_chunk(const float* acc) {
   }
 }
 
-template <bool BF16, int KMAX, int CH>
+// One wave per (token, block of 64 x CH chunks of the row): the token's k
+// dispatched rows and the shared slabs are summed as RMAX source rows, all
+// loads of a block issued before any is accumulated (one memory round trip),
+// and small batches spread each row over several waves.
+template <bool BF16, int RMAX, int CH>
 __global__ __launch_bounds__(256) void k_combine(const u32x4_t* __restrict__ y, int64_t T, int row_chunks, int k,
                                                  const int32_t* __restrict__ inv, const float* __restrict__ w,
                                                  const u32x4_t* __restrict__ shared, int n_shared,
                                                  u32x4_t* __restrict__ out) {
   constexpr int EPC = BF16 ? 8 : 4;   // elements per 16-byte chunk
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave; t < T; t += stride) {
+  constexpr int BLK = 64 * CH;        // chunks per work item
+  const int lane = threadIdx.x & 63;
+  const int nblk = (row_chunks + BLK - 1) / BLK;
+  const int64_t items = T * nblk;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); it < items; it += nwaves) {
+    const int64_t t = it / nblk;
+    const int c_begin = static_cast<int>(it % nblk) * BLK;
     const int my_pos = lane < k ? inv[t * k + lane] : -1;
     const float my_w = lane < k ? w[t * k + lane] : 0.f;
-    int pos[KMAX];
-    float wt[KMAX];
+    // source rows: j < k the dispatched rows (skipped if not local), then the
+    // shared slabs with weight 1; wave-uniform.
+    const u32x4_t* src[RMAX];
+    float wt[RMAX];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      pos[j] = __shfl(my_pos, j, kWave);
-      wt[j] = __shfl(my_w, j, kWave);
+    for (int j = 0; j < RMAX; ++j) {
+      const int pj = __shfl(my_pos, j < k ? j : 0, kWave);
+      const float wj = __shfl(my_w, j < k ? j : 0, kWave);
+      if (j < k) {
+        src[j] = pj >= 0 ? y + static_cast<int64_t>(pj) * row_chunks : nullptr;
+        wt[j] = wj;
+      } else if (j < k + n_shared) {
+        src[j] = shared + (static_cast<int64_t>(j - k) * T + t) * row_chunks;
+        wt[j] = 1.f;
+      } else {
+        src[j] = nullptr;
+        wt[j] = 0.f;
+      }
     }
-    for (int c0 = 0; c0 < row_chunks; c0 += 64 * CH) {
-      u32x4_t v[KMAX][CH];
-      // Issue every source row's loads before accumulating any of them
-      // (pos[j] is uniform across the wave, so the branches do not diverge).
+    u32x4_t v[RMAX][CH];
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (pos[j] >= 0) {
+    for (int j = 0; j < RMAX; ++j) {
+      if (src[j]) {
 #pragma unroll
-          for (int c = 0; c < CH; ++c) {
-            const int ci = c0 + c * 64 + lane;
-            if (ci < row_chunks) v[j][c] = y[static_cast<int64_t>(pos[j]) * row_chunks + ci];
-          }
+        for (int c = 0; c < CH; ++c) {
+          const int ci = c_begin + c * 64 + lane;
+          if (ci < row_chunks) v[j][c] = src[j][ci];
         }
       }
-      float acc[CH][EPC];
+    }
+    float acc[CH][EPC];
 #pragma unroll
-      for (int c = 0; c < CH; ++c)
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[c][e] = 0.f;
+      for (int e = 0; e < EPC; ++e) acc[c][e] = 0.f;
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (pos[j] >= 0) {
+    for (int j = 0; j < RMAX; ++j) {
+      if (src[j]) {
 #pragma unroll
-          for (int c = 0; c < CH; ++c) acc_chunk<BF16>(acc[c], v[j][c], wt[j]);
-        }
+        for (int c = 0; c < CH; ++c) acc_chunk<BF16>(acc[c], v[j][c], wt[j]);
       }
+    }
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int ci = c0 + c * 64 + lane;
-        if (ci < row_chunks) {
-          for (int sl = 0; sl < n_shared; ++sl)
-            acc_chunk<BF16>(acc[c], shared[(sl * T + t) * row_chunks + ci], 1.0f);
-          out[t * row_chunks + ci] = pack_chunk<BF16>(acc[c]);
-        }
-      }
+    for (int c = 0; c < CH; ++c) {
+      const int ci = c_begin + c * 64 + lane;
+      if (ci < row_chunks) out[t * row_chunks + ci] = pack_chunk<BF16>(acc[c]);
     }
   }
 }
 
+// Rows per token = k + shared slabs (at most 32).  Two chunks per lane when
+// there are enough tokens to fill the GPU, one otherwise.
 template <bool BF16>
-static void launch_k(int kmax, dim3 g, hipStream_t s, const u32x4_t* y, int64_t T, int rc, int k,
+static void launch_k(int rows, int64_t T, int rc, int64_t max_blocks, hipStream_t s, const u32x4_t* y, int k,
                      const int32_t* inv, const float* w, const u32x4_t* sh, int nsh, u32x4_t* out) {
-  if (kmax <= 4)
-    hipLaunchKernelGGL((k_combine<BF16, 4, 4>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, nsh, out);
-  else if (kmax <= 8)
+  const bool wide = T * ((rc + 127) / 128) >= 4096;
+  const int blk = wide && rows <= 8 ? 128 : 64;
+  int64_t blocks = (T * ((rc + blk - 1) / blk) + 3) / 4;
+  if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
+  const dim3 g(static_cast<unsigned>(blocks));
+  if (rows <= 8 && blk == 128)
     hipLaunchKernelGGL((k_combine<BF16, 8, 2>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, nsh, out);
-  else
+  else if (rows <= 8)
+    hipLaunchKernelGGL((k_combine<BF16, 8, 1>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, nsh, out);
+  else if (rows <= 16)
     hipLaunchKernelGGL((k_combine<BF16, 16, 1>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, nsh, out);
+  else
+    hipLaunchKernelGGL((k_combine<BF16, 32, 1>), g, dim3(256), 0, s, y, T, rc, k, inv, w, sh, nsh, out);
 }
 
 moe_status launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return MOE_OK;
   const int rc = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
-  int64_t blocks = (a.T + 3) / 4;
-  if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
-  const dim3 g(static_cast<unsigned>(blocks));
   const auto* y = static_cast<const u32x4_t*>(a.y);
   const auto* sh = static_cast<const u32x4_t*>(a.shared);
   auto* out = static_cast<u32x4_t*>(a.out);
   const int nsh = sh ? (a.n_shared > 0 ? a.n_shared : 1) : 0;
+  if (a.k + nsh > 32) return MOE_ERR_UNSUPPORTED;
   if (a.act == MOE_BF16)
-    launch_k<true>(a.k, g, s, y, a.T, rc, a.k, a.inv, a.w, sh, nsh, out);
+    launch_k<true>(a.k + nsh, a.T, rc, a.max_blocks, s, y, a.k, a.inv, a.w, sh, nsh, out);
   else
-    launch_k<false>(a.k, g, s, y, a.T, rc, a.k, a.inv, a.w, sh, nsh, out);
+    launch_k<false>(a.k + nsh, a.T, rc, a.max_blocks, s, y, a.k, a.inv, a.w, sh, nsh, out);
   DBOMOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -101,6 +101,8 @@ moe_status check_desc(const moe_layer_desc* d) {
     if (st != MOE_OK) return st;
     if (!d->shared_w13 || !d->shared_w2) return MOE_ERR_INVALID_ARG;
     if (!aligned16(d->shared_w13) || !aligned16(d->shared_w2)) return MOE_ERR_MISALIGNED;
+    // the combine sums k routed rows and the shared down projection's slabs
+    if (d->route.k + dense_down_chunks(d->act, d->shared_I, d->I) > 32) return MOE_ERR_UNSUPPORTED;
   }
   return MOE_OK;
 }
