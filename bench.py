@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="layer configuration 1..5 (default 2)")
     ap.add_argument("--schedule", default="dbo", choices=["dbo", "serial", "unsplit", "dbo_late_event"])
     ap.add_argument("--comm-cu-budget", type=int, default=0)
+    ap.add_argument("--ffn-tile-m", type=int, default=0,
+                    help="expert FFN row tile: 0 automatic, 16 weight-streaming kernel, 32/64/128 LDS-tiled kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -152,7 +154,7 @@ def main():
     T = cfg.T
 
     def run(sched):
-        L.run(sched, comm_cu_budget=args.comm_cu_budget)
+        L.run(sched, comm_cu_budget=args.comm_cu_budget, ffn_tile_m=args.ffn_tile_m)
 
     def timed(sched):
         for _ in range(Wm):
@@ -205,8 +207,8 @@ def main():
     roof["traffic"] = traffic
     T_mb0 = halves[0][1] - halves[0][0]
     I_sh = cfg.n_shared * cfg.shared_I
-    tile = B.moe_ffn_auto_tile(B.dtype_code(L.x), B.dtype_code(L.w13), cfg.H, cfg.I, -(-T_mb0 * cfg.k // cfg.E),
-                               T_mb0 if I_sh else 0, I_sh)
+    tile = args.ffn_tile_m or B.moe_ffn_auto_tile(B.dtype_code(L.x), B.dtype_code(L.w13), cfg.H, cfg.I,
+                                                  -(-T_mb0 * cfg.k // cfg.E), T_mb0 if I_sh else 0, I_sh)
     kname = ("k_gemm_nt_f32 (fp32 SIMT)" if cfg.act == "f32" else
              "k_gemm_ws (weight-streaming, 16-row tiles)" if tile == 16 else f"k_gemm_nt ({tile}-row LDS tiles)")
     roof["kernel"] = f"gate/up expert GEMM + SwiGLU, routed and shared experts: {kname}, MODE_GATEUP"

@@ -11,7 +11,8 @@
 //  1. count   - one workgroup per 256 pairs: LDS histogram of local experts;
 //               flags ids outside [0, E).
 //  2. scan    - one workgroup: per expert, exclusive prefix over the blocks
-//               (stable block bases), then counts -> offsets (and tile offsets).
+//               (stable block bases; several threads per expert, each over a
+//               run of blocks), then counts -> offsets (and tile offsets).
 //  3. rank    - one workgroup per 256 pairs: stable rank of every pair inside its
 //               block from wave ballots (lanes holding the same expert are
 //               grouped with a ballot loop; rank = popcount of lower lanes) plus
@@ -96,7 +97,10 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wsum) {
   return r;
 }
 
-__global__ __launch_bounds__(1024) void k_disp_scan(int64_t nb, int E_loc, int tile_m,
+// TPE threads per expert (TPE * E_loc <= 1024): thread (e, part) owns a
+// contiguous run of blocks of expert column e, so every load is independent
+// and coalesced across experts; the per-part sums are scanned in LDS.
+__global__ __launch_bounds__(1024) void k_disp_scan(int64_t nb, int E_loc, int tpe, int tile_m,
                                                     int32_t* __restrict__ block_hist,
                                                     const int32_t* __restrict__ block_err,
                                                     int32_t* __restrict__ counts,
@@ -104,31 +108,56 @@ __global__ __launch_bounds__(1024) void k_disp_scan(int64_t nb, int E_loc, int t
                                                     int32_t* __restrict__ tile_offsets,
                                                     int32_t* __restrict__ err) {
   __shared__ int s_wsum[32];
-  const int e = threadIdx.x;
-  int cnt = 0;
-  if (e < E_loc) {
-    for (int64_t b = 0; b < nb; ++b) {
-      const int64_t i = b * E_loc + e;
-      const int v = block_hist[i];
-      block_hist[i] = cnt;
-      cnt += v;
-    }
-    counts[e] = cnt;
+  __shared__ int s_part[1024];          // [part][e] sums, then their exclusive prefix
+  __shared__ int s_total[kMaxELoc];
+  const int tid = threadIdx.x;
+  const bool active = tid < tpe * E_loc;
+  const int e = tid % E_loc;
+  const int part = tid / E_loc;
+  const int64_t per = (nb + tpe - 1) / tpe;
+  const int64_t b0 = active ? min(nb, part * per) : 0;
+  const int64_t b1 = active ? min(nb, b0 + per) : 0;
+  constexpr int U = 8;
+  int sum = 0;
+  for (int64_t b = b0; b < b1; b += U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = b + u < b1 ? block_hist[(b + u) * E_loc + e] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) sum += v[u];
   }
+  if (active) s_part[part * E_loc + e] = sum;
+  __syncthreads();
+  int base = 0;
+  if (active)
+    for (int q = 0; q < part; ++q) base += s_part[q * E_loc + e];
+  if (active && part == tpe - 1) s_total[e] = base + sum;
+  // rewrite the blocks with their stable base inside the expert
+  for (int64_t b = b0; b < b1; b += U) {
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = b + u < b1 ? block_hist[(b + u) * E_loc + e] : 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (b + u < b1) block_hist[(b + u) * E_loc + e] = base;
+      base += v[u];
+    }
+  }
+  int any = 0;
+  for (int64_t b = tid; b < nb; b += 1024) any |= block_err[b];
+  any = __syncthreads_or(any);
+  const int cnt = tid < E_loc ? s_total[tid] : 0;
+  if (tid < E_loc) counts[tid] = cnt;
   const int off = block_excl_scan_1024(cnt, s_wsum);
-  if (e < E_loc) offsets[e] = off;
-  if (e == E_loc - 1) offsets[E_loc] = off + cnt;
+  if (tid < E_loc) offsets[tid] = off;
+  if (tid == E_loc - 1) offsets[E_loc] = off + cnt;
   if (tile_offsets) {
     const int tiles = (cnt + tile_m - 1) / tile_m;
     const int toff = block_excl_scan_1024(tiles, s_wsum);
-    if (e < E_loc) tile_offsets[e] = toff;
-    if (e == E_loc - 1) tile_offsets[E_loc] = toff + tiles;
+    if (tid < E_loc) tile_offsets[tid] = toff;
+    if (tid == E_loc - 1) tile_offsets[E_loc] = toff + tiles;
   }
-  if (threadIdx.x == 0) {
-    int any = 0;
-    for (int64_t b = 0; b < nb; ++b) any |= block_err[b];
-    err[0] = any;
-  }
+  if (tid == 0) err[0] = any;
 }
 
 __global__ __launch_bounds__(256) void k_disp_rank(const int32_t* __restrict__ ids, int64_t n_pairs,
@@ -213,7 +242,9 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
                        a.E_total, a.e_begin, E_loc, w.block_hist, w.block_err);
     DBOMOE_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(k_disp_scan, dim3(1), dim3(1024), 0, s, nb, E_loc, a.tile_m > 0 ? a.tile_m : 1,
+  int tpe = 1;
+  while (tpe * 2 * E_loc <= 1024 && tpe * 2 <= nb) tpe *= 2;
+  hipLaunchKernelGGL(k_disp_scan, dim3(1), dim3(1024), 0, s, nb, E_loc, tpe, a.tile_m > 0 ? a.tile_m : 1,
                      w.block_hist, w.block_err, a.counts, a.offsets,
                      a.tile_m > 0 ? a.tile_offsets : nullptr, w.err);
   DBOMOE_CHECK_LAUNCH();

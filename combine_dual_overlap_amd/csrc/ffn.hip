@@ -12,15 +12,18 @@
 namespace dbomoe {
 
 // Rows per expert under roughly uniform routing are about Poisson(mean): size
-// the row tile for the likely largest expert.  Up to 32 rows the weights
-// dominate the bytes: the weight-streaming kernel (16-row tiles) where every K
-// fits its activation tile, else the 32-row LDS-tiled kernel; beyond that the
-// LDS-tiled kernel with 64- or 128-row tiles (prefill).
-static int choose_tile_m(int64_t mean_rows, bool ws_fits) {
+// the row tile for the likely largest expert, so most experts take one row
+// tile (their weights stream once) and large experts get the big MFMA tile.
+// Measured on the five layer shapes (DBO schedule): 32-row tiles for decode,
+// 64 up to about 96 rows, 128 beyond.  The weight-streaming kernel (16-row
+// tiles) is faster in isolation when every expert holds at most 16 rows, but
+// splits the Poisson tail of 17-32-row experts into two tiles, and loses to
+// the 32-row LDS-tiled kernel inside the layer; it is used only on request.
+static int choose_tile_m(int64_t mean_rows) {
   const double m = static_cast<double>(mean_rows);
   const double est_max = m + 3.0 * std::sqrt(m) + 1.0;
-  if (est_max <= 32) return ws_fits ? 16 : 32;
-  if (est_max <= 64) return 64;
+  if (est_max <= 32) return 32;
+  if (est_max <= 96) return 64;
   return 128;
 }
 
@@ -129,9 +132,8 @@ moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.act == MOE_F32) return launch_ffn_f32(a, s);
   const bool fp8 = a.wdt == MOE_FP8_E4M3FN;
   const bool dense = a.offsets == nullptr;
-  const bool ws_fits = ffn_ws_fits(a.act, a.H, a.I, a.rows1, a.I1);
-  if (a.tile_m == 16 && !ws_fits) return MOE_ERR_UNSUPPORTED;
-  const int bm = a.tile_m > 0 ? a.tile_m : choose_tile_m(a.rows_hint, ws_fits);
+  if (a.tile_m == 16 && !ffn_ws_fits(a.act, a.H, a.I, a.rows1, a.I1)) return MOE_ERR_UNSUPPORTED;
+  const int bm = a.tile_m > 0 ? a.tile_m : choose_tile_m(a.rows_hint);
 
   GemmParams p1{};
   p1.offsets = a.offsets;
@@ -218,7 +220,7 @@ extern "C" int32_t moe_ffn_auto_tile(moe_dtype act, moe_dtype wdt, int32_t H, in
       rows_per_expert < 0 || rows1 < 0 || (rows1 > 0 && I1 <= 0))
     return 0;
   if (act == MOE_F32) return 32;
-  return choose_tile_m(rows_per_expert, ffn_ws_fits(act, H, I, rows1, I1));
+  return choose_tile_m(rows_per_expert);
 }
 
 extern "C" size_t moe_ffn_workspace_size(int64_t cap_rows, int32_t I, moe_dtype act) {

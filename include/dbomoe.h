@@ -153,8 +153,9 @@ size_t moe_ffn_workspace_size(int64_t cap_rows, int32_t I, moe_dtype act);
  * rows_per_expert rows (dbo_moe_layer passes ceil(T*k/E)); rows1/I1 describe
  * a dense group run in the same launches (the shared experts of
  * dbo_moe_layer: rows1 = microbatch tokens, I1 = shared_I), 0/0 if none.
- * Returns 16 (weight-streaming kernel), 32, 64 or 128 (LDS-tiled kernel), or
- * 0 for shapes moe_grouped_ffn rejects.  Pure host function. */
+ * Returns 32, 64 or 128 (LDS-tiled kernel; the automatic choice never takes
+ * the weight-streaming kernel), or 0 for shapes moe_grouped_ffn rejects.
+ * Pure host function. */
 int32_t moe_ffn_auto_tile(moe_dtype act, moe_dtype wdt, int32_t H, int32_t I, int64_t rows_per_expert,
                           int64_t rows1, int32_t I1);
 moe_status moe_grouped_ffn(const void* x_perm, moe_dtype act, int32_t H, int32_t I,

@@ -72,10 +72,11 @@ def test_layer_workspace_size_and_validation():
 
 def test_ffn_auto_tile_choice():
     from combine_dual_overlap_amd import binding as B
-    # decode-sized experts with H, I <= 2048: the weight-streaming kernel
-    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_BF16, 2048, 1408, 12, 128, 2816) == 16
-    # the same rows with H = 7168: the activation tile no longer fits LDS
+    # decode-sized experts (Poisson(12) rows: the largest fits 32)
+    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_BF16, 2048, 1408, 12, 128, 2816) == 32
     assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 7168, 2048, 12) == 32
+    # about 64 rows per expert
+    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 7168, 2048, 64) == 64
     # prefill-sized experts
     assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 2048, 768, 256) == 128
     assert B.moe_ffn_auto_tile(B.MOE_F32, B.MOE_F32, 128, 256, 8) == 32
