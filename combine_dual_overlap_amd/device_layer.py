@@ -69,7 +69,6 @@ class DeviceLayer:
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=d)
         self.out = torch.empty_like(self.x)
         self.ctx = B.DboContext()
-        self.compute = torch.cuda.current_stream(d)
         self.comm = torch.cuda.Stream(device=d)
 
     def run(self, schedule: str = "dbo", min_tokens_to_split: int = 2, split_at: int = -1,
@@ -78,7 +77,10 @@ class DeviceLayer:
         out = self.out if out is None else out
         forced = self.forced_ids if forced_ids is None else forced_ids
         opts = B.dbo_opts(B.SCHEDULES[schedule], min_tokens_to_split, split_at, comm_cu_budget, ffn_tile_m)
-        B.dbo_moe_layer(self.ctx, self.desc, x, out, opts, self.ws, self.compute, self.comm,
+        # the compute stream is the caller's current stream (also under graph
+        # capture); the comm stream joins it through the layer's events
+        compute = torch.cuda.current_stream(self.device)
+        B.dbo_moe_layer(self.ctx, self.desc, x, out, opts, self.ws, compute, self.comm,
                         forced_ids=forced, logit_bias=self.logit_bias)
         return out
 

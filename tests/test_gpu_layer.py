@@ -155,7 +155,7 @@ def test_layer_workspace_too_small_is_rejected():
     small = L.ws[: L.ws.numel() // 2]
     opts = C.binding.dbo_opts(C.binding.DBO_SCHED_DBO, 2, -1, 0, 0)
     with pytest.raises(C.binding.MoEError) as e:
-        C.binding.dbo_moe_layer(L.ctx, L.desc, L.x, L.out, opts, small, L.compute, L.comm)
+        C.binding.dbo_moe_layer(L.ctx, L.desc, L.x, L.out, opts, small, torch.cuda.current_stream(), L.comm)
     assert e.value.status == C.binding.MOE_ERR_WORKSPACE
 
 
@@ -173,3 +173,40 @@ def test_timing_events_report_ffn_times():
     L.ctx.set_timing(False)
     L.run("dbo")
     assert L.ctx.ffn_times() == t2            # untimed calls leave the record alone
+
+
+@pytest.mark.parametrize("cid", [2, 3, 5])
+@pytest.mark.parametrize("schedule", ["dbo", "serial"])
+def test_layer_captured_in_a_graph_replays_exactly(cid, schedule):
+    """dbo_moe_layer under stream capture (the comm stream joins the capture
+    through the layer's events; device-side counts, no host sync): every
+    replay, with eager layer calls in between, equals the eager output bit for
+    bit, and the eager output is within tolerance of the oracle."""
+    inp, ov = inputs(cid, True)
+    cfg = inp["cfg"]
+    L = _layer(inp)
+    eager = L.run(schedule).clone()
+    torch.cuda.synchronize()
+    ref = O.moe_layer_expert(ov)
+    print(f"graph cfg={cfg.name} schedule={schedule}", flush=True)
+    assert_close(to_f64(eager), ref["out"], tol_for(cfg), "eager", ref["scale"])
+    out = torch.empty_like(L.out)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        L.run(schedule, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.run(schedule, out=out)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        other = L.run("unsplit" if rep % 2 else schedule).clone()   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(other.float()).all()
+    del g
