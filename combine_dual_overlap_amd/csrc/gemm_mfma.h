@@ -329,23 +329,30 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
 
   const int frag_row = lane & 15;
   const int frag_c = lane >> 4;             // 16-byte chunk within the 32-wide K step
+  // 16-row subtiles of this wave that hold rows of the expert: the last row
+  // tile of an expert is usually partial, and its empty subtiles skip their
+  // LDS reads and MFMAs (a wave-uniform count).
+  const int tm_valid = __builtin_amdgcn_readfirstlane(
+      max(0, min(TM, (t.rows - t.m_off - wm * WM + 15) / 16)));
   auto compute_stage = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 32; ++kk) {
       bf16x8_t af[TM], bfv[TN];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
-        af[tm] = *reinterpret_cast<const bf16x8_t*>(
-            &sA[buf][lds_off(wm * WM + tm * 16 + frag_row, kk * 4 + frag_c)]);
+        if (tm < tm_valid)
+          af[tm] = *reinterpret_cast<const bf16x8_t*>(
+              &sA[buf][lds_off(wm * WM + tm * 16 + frag_row, kk * 4 + frag_c)]);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
         bfv[tn] = *reinterpret_cast<const bf16x8_t*>(
             &sB[buf][lds_off(b_lds_row<MODE, WN, TN>(wn, tn) + frag_row, kk * 4 + frag_c)]);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
+        if (tm < tm_valid)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfv[tn], acc[tm][tn], 0, 0, 0);
+          for (int tn = 0; tn < TN; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfv[tn], acc[tm][tn], 0, 0, 0);
     }
   };
 
