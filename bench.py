@@ -84,6 +84,44 @@ def gateup_work(cfg, counts_per_mb, rows_per_mb):
     return out
 
 
+def shared_slabs(cfg) -> int:
+    """Slabs the shared experts' down projection writes (the library cuts it
+    into K chunks of at most about I, each a multiple of 64)."""
+    I1 = cfg.n_shared * cfg.shared_I
+    if not I1 or cfg.act == "f32":
+        return 1 if I1 else 0
+    for d in range(-(-I1 // cfg.I), 1, -1):
+        if I1 % (d * 64) == 0:
+            return d
+    return 1
+
+
+def comm_work(cfg, L, halves, comm_ms):
+    """Achieved HBM bandwidth of the dispatch step (count, scan, rank, gather)
+    and of the combine, from their algorithmic bytes per microbatch: dispatch
+    reads every token row with a local expert once and writes its dispatched
+    rows (plus ids, perm and inv); combine reads the dispatched rows, the
+    shared slabs, ids and weights, and writes every token row."""
+    import torch
+    s = 4 if cfg.act == "f32" else 2
+    d_bytes, c_bytes = [], []
+    for mb, (a, b) in enumerate(halves):
+        n = b - a
+        inv = L.view(mb, "inv", torch.int32, (n * cfg.k,), T=cfg.T).cpu().numpy().reshape(n, cfg.k)
+        M = int((inv >= 0).sum())
+        t_hit = int((inv >= 0).any(axis=1).sum())
+        d_bytes.append(t_hit * cfg.H * s + M * cfg.H * s + 4 * n * cfg.k + 4 * M + 4 * n * cfg.k)
+        c_bytes.append(M * cfg.H * s + 8 * n * cfg.k + n * cfg.H * s + shared_slabs(cfg) * n * cfg.H * s)
+    out = {"schedule": "serial"}
+    for name, cols, byts in (("dispatch", [0, 1], d_bytes), ("combine", [2, 3], c_bytes)):
+        ms = comm_ms[:, cols[:len(halves)]]
+        avg_s = float(ms[ms > 0].mean()) / 1e3
+        gbs = float(np.mean(byts)) / avg_s / 1e9
+        out[name] = {"avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": int(np.mean(byts)),
+                     "achieved_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def cpu_baseline(inp, cfg, budget_s: float):
     """The oracle (as it stands) on a bounded sample of the same workload:
     its first tokens (all of them when one run fits the budget)."""
@@ -210,6 +248,15 @@ def main():
     dn_ms = times[:, [1, 3]]
     dn_ms = dn_ms[dn_ms > 0]
 
+    # Dispatch and combine timed in the SERIAL schedule (nothing runs beside
+    # them there), against their algorithmic bytes.
+    L.ctx.set_timing(True)
+    for _ in range(n_t):
+        run("serial")
+    torch.cuda.synchronize()
+    comm = np.array([L.ctx.comm_times(b) for b in range(n_t)])     # [n, 4] ms
+    L.ctx.set_timing(False)
+
     T0 = L.ctx.last_stats()["T0"]
     halves = [(0, T0), (T0, T)] if T0 < T else [(0, T)]
     counts = [L.view(mb, "counts", torch.int32, (cfg.E_loc,), T=T).cpu().numpy() for mb in range(len(halves))]
@@ -240,6 +287,8 @@ def main():
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
     roof["algorithmic_bytes_per_launch"] = int(bytes_launch)
     roof["algorithmic_flops_per_launch"] = int(flops_launch)
+
+    comm_rec = comm_work(cfg, L, halves, comm)
 
     base = None
     if not args.no_cpu_baseline:
@@ -273,6 +322,7 @@ def main():
         "serial_tokens_per_s": round(T * K / dt_serial, 1),
         "unsplit_tokens_per_s": round(T * K / dt_unsplit, 1),
         "dbo_speedup_vs_serial": round(dt_serial_graph / dt_graph, 4),
+        "comm_steps": comm_rec,
         "dbo_speedup_vs_serial_eager": round(dt_serial / dt, 4),
         "kernel_ms": {"gate_up_avg": round(float(np.mean(gu_ms)), 4), "down_avg": round(float(np.mean(dn_ms)), 4)},
         "roofline": roof,

@@ -25,7 +25,8 @@ SCHEDULES = {"unsplit": 0, "serial": 1, "dbo": 2, "dbo_late_event": 3}
 EXPORTED = [
     "moe_route_workspace_size", "moe_route_topk", "moe_dispatch_workspace_size", "moe_dispatch",
     "moe_get_device_error", "moe_ffn_workspace_size", "moe_ffn_auto_tile", "moe_grouped_ffn", "moe_combine",
-    "dbo_ctx_create", "dbo_ctx_destroy", "dbo_ctx_set_timing", "dbo_ctx_ffn_times", "dbo_ctx_last_stats",
+    "dbo_ctx_create", "dbo_ctx_destroy", "dbo_ctx_set_timing", "dbo_ctx_ffn_times", "dbo_ctx_comm_times",
+    "dbo_ctx_last_stats",
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "dbo_moe_layer", "moe_status_string",
 ]
 
@@ -88,6 +89,7 @@ def lib():
             "dbo_ctx_destroy": (None, [_vp]),
             "dbo_ctx_set_timing": (_i32, [_vp, _i32]),
             "dbo_ctx_ffn_times": (_i32, [_vp, _i32, ctypes.POINTER(ctypes.c_float)]),
+            "dbo_ctx_comm_times": (_i32, [_vp, _i32, ctypes.POINTER(ctypes.c_float)]),
             "dbo_ctx_last_stats": (_i32, [_vp, ctypes.POINTER(_i64)]),
             "moe_layer_workspace_size": (_sz, [ctypes.POINTER(moe_layer_desc), _i64]),
             "moe_layer_workspace_layout": (_i32, [ctypes.POINTER(moe_layer_desc), _i64, _i32,
@@ -232,6 +234,12 @@ class DboContext:
         """[A gate/up, A down, B gate/up, B down] ms of the timed call `back` calls ago."""
         ms = (ctypes.c_float * 4)()
         _check(lib().dbo_ctx_ffn_times(self.handle, back, ms), "dbo_ctx_ffn_times")
+        return list(ms)
+
+    def comm_times(self, back: int = 0):
+        """[A dispatch, B dispatch, A combine, B combine] ms of the timed call `back` calls ago."""
+        ms = (ctypes.c_float * 4)()
+        _check(lib().dbo_ctx_comm_times(self.handle, back, ms), "dbo_ctx_comm_times")
         return list(ms)
 
     def last_stats(self) -> dict:

@@ -22,8 +22,9 @@ constexpr int kTimingRing = 128;   // timed calls remembered by a context
 struct dbo_ctx {
   hipEvent_t ev[dbomoe::sched::kNumEvents] = {};
   hipEvent_t join = nullptr;
-  // Timing events, created when timing is first enabled: [call slot][microbatch][3]
-  hipEvent_t (*tev)[2][3] = nullptr;
+  // Timing events, created when timing is first enabled: [call slot][microbatch][7]
+  // (FFN start / between the GEMMs / end, dispatch start / end, combine start / end)
+  hipEvent_t (*tev)[2][7] = nullptr;
   bool (*timed)[2] = nullptr;
   bool timing = false;
   int64_t timed_calls = 0;
@@ -149,7 +150,10 @@ struct HipBackend {
                        d->expert_end, 0, buf<int32_t>(mb, B_COUNTS), buf<int32_t>(mb, B_OFFSETS),
                        nullptr, buf<int32_t>(mb, B_PERM), buf<int32_t>(mb, B_INV),
                        buf<void>(mb, B_XPERM), buf<void>(mb, B_DISPWS), o->comm_cu_budget};
+        if (ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][3], s) != hipSuccess) return MOE_ERR_HIP;
         st = launch_dispatch(a, s);
+        if (st == MOE_OK && ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][4], s) != hipSuccess)
+          return MOE_ERR_HIP;
         break;
       }
       case sched::kFfn: {
@@ -195,7 +199,10 @@ struct HipBackend {
         CombineArgs a{buf<void>(mb, B_YPERM), d->act, T, d->H, k, buf<int32_t>(mb, B_INV), buf<float>(mb, B_W),
                       d->shared_I > 0 ? buf<void>(mb, B_SHOUT) : nullptr, out + row0[mb] * d->H * as,
                       o->comm_cu_budget, d->shared_I > 0 ? dense_down_chunks(d->act, d->shared_I, d->I) : 0};
+        if (ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][5], s) != hipSuccess) return MOE_ERR_HIP;
         st = launch_combine(a, s);
+        if (st == MOE_OK && ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][6], s) != hipSuccess)
+          return MOE_ERR_HIP;
         break;
       }
       default:
@@ -256,7 +263,7 @@ extern "C" void dbo_ctx_destroy(dbo_ctx* c) {
   if (c->tev) {
     for (int r = 0; r < kTimingRing; ++r)
       for (int m = 0; m < 2; ++m)
-        for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < 7; ++j)
           if (c->tev[r][m][j]) (void)hipEventDestroy(c->tev[r][m][j]);
     delete[] c->tev;
     delete[] c->timed;
@@ -267,11 +274,11 @@ extern "C" void dbo_ctx_destroy(dbo_ctx* c) {
 extern "C" moe_status dbo_ctx_set_timing(dbo_ctx* c, int32_t enable) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (enable && !c->tev) {
-    c->tev = new hipEvent_t[kTimingRing][2][3]();
+    c->tev = new hipEvent_t[kTimingRing][2][7]();
     c->timed = new bool[kTimingRing][2]();
     for (int r = 0; r < kTimingRing; ++r)
       for (int m = 0; m < 2; ++m)
-        for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < 7; ++j)
           if (hipEventCreate(&c->tev[r][m][j]) != hipSuccess) return MOE_ERR_HIP;
   }
   c->timing = enable != 0;
@@ -288,6 +295,20 @@ extern "C" moe_status dbo_ctx_ffn_times(dbo_ctx* c, int32_t back, float* ms4) {
     if (hipEventSynchronize(c->tev[r][m][2]) != hipSuccess) return MOE_ERR_HIP;
     if (hipEventElapsedTime(&ms4[2 * m], c->tev[r][m][0], c->tev[r][m][1]) != hipSuccess) return MOE_ERR_HIP;
     if (hipEventElapsedTime(&ms4[2 * m + 1], c->tev[r][m][1], c->tev[r][m][2]) != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status dbo_ctx_comm_times(dbo_ctx* c, int32_t back, float* ms4) {
+  if (!c || !ms4 || back < 0) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i) ms4[i] = 0.f;
+  if (!c->tev || back >= kTimingRing || back >= c->timed_calls) return MOE_OK;
+  const int r = static_cast<int>(((c->timed_calls - 1 - back) % kTimingRing + kTimingRing) % kTimingRing);
+  for (int m = 0; m < 2; ++m) {
+    if (!c->timed[r][m]) continue;
+    if (hipEventSynchronize(c->tev[r][m][6]) != hipSuccess) return MOE_ERR_HIP;
+    if (hipEventElapsedTime(&ms4[m], c->tev[r][m][3], c->tev[r][m][4]) != hipSuccess) return MOE_ERR_HIP;
+    if (hipEventElapsedTime(&ms4[2 + m], c->tev[r][m][5], c->tev[r][m][6]) != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
 }

@@ -229,14 +229,18 @@ moe_status dbo_ctx_create(dbo_ctx** ctx);
 void dbo_ctx_destroy(dbo_ctx* ctx);
 /* Optional kernel timing: while enabled, each dbo_moe_layer call brackets
  * each microbatch's two expert GEMM kernels with timing events on the compute
- * stream (the context remembers the last 128 timed calls; the events are
- * created by the first enable). */
+ * stream, and its dispatch and combine kernels on the stream they run on (the
+ * context remembers the last 128 timed calls; the events are created by the
+ * first enable). */
 moe_status dbo_ctx_set_timing(dbo_ctx* ctx, int32_t enable);
 /* Elapsed ms of the expert GEMM kernels of the timed call `back` calls ago
  * (0 = the last), ms4 = {A gate/up, A down, B gate/up, B down}; zeros for a
  * microbatch that did not run or a call not remembered.  Waits for the end
  * events of that call. */
 moe_status dbo_ctx_ffn_times(dbo_ctx* ctx, int32_t back, float* ms4);
+/* The same for the comm-side steps: ms4 = {A dispatch, B dispatch, A combine,
+ * B combine} (each step's kernels from the first launch to the last). */
+moe_status dbo_ctx_comm_times(dbo_ctx* ctx, int32_t back, float* ms4);
 /* Schedule bookkeeping of the last call: stats[0..5] = {schedule run, T0,
  * yields A, yields B, stages launched, events recorded}. */
 moe_status dbo_ctx_last_stats(dbo_ctx* ctx, int64_t* stats6);

@@ -166,9 +166,13 @@ def test_timing_events_report_ffn_times():
     L.run("dbo")
     t = L.ctx.ffn_times()
     assert all(v > 0 for v in t), t
+    c = L.ctx.comm_times()
+    assert all(v > 0 for v in c), c
     L.run("unsplit")
     t2 = L.ctx.ffn_times()
     assert t2[0] > 0 and t2[1] > 0 and t2[2:] == [0.0, 0.0]
+    c2 = L.ctx.comm_times()
+    assert c2[0] > 0 and c2[2] > 0 and c2[1] == 0.0 and c2[3] == 0.0
     assert L.ctx.ffn_times(1)[2] > 0          # the earlier DBO call is still remembered
     L.ctx.set_timing(False)
     L.run("dbo")
