@@ -7,7 +7,8 @@
 // rows ("DeepEP HT: full decode CUDA graphs via worst-token dispatch", bot
 // review 2), so nothing waits on the host.
 //
-// Four kernels, each a pass over HBM-resident data:
+// Four kernels, each a pass over HBM-resident data (small batches fuse the
+// first three into one workgroup, k_disp_small):
 //  1. count   - one workgroup per 256 pairs: LDS histogram of local experts;
 //               flags ids outside [0, E).
 //  2. scan    - one workgroup: per expert, exclusive prefix over the blocks
@@ -200,6 +201,96 @@ __global__ __launch_bounds__(256) void k_disp_rank(const int32_t* __restrict__ i
   }
 }
 
+// Small batches (few pairs, E_loc <= 256): count, scan and rank in one
+// workgroup, so the dispatch is two launches (this and the gather) instead of
+// four.  Pairs are taken 1024 at a time in order; inside a chunk a pair's
+// stable rank is its rank among same-expert lanes of its wave (ballot groups)
+// plus the counts of the lower waves, on top of the expert's running count.
+constexpr int kSmallChunk = 1024;
+constexpr int kSmallMaxPairs = 8192;
+constexpr int kSmallMaxELoc = 256;
+
+__global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__ ids, int64_t n_pairs,
+                                                     int E_total, int e_begin, int E_loc, int tile_m,
+                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ tile_offsets,
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                     int32_t* __restrict__ err) {
+  __shared__ int s_hist[kSmallMaxELoc];
+  __shared__ int s_run[kSmallMaxELoc];      // offsets, then offsets + pairs ranked so far
+  __shared__ int s_wcnt[16][kSmallMaxELoc]; // this chunk's count per wave and expert
+  __shared__ int s_wsum[32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E_loc; e += 1024) s_hist[e] = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int64_t p = tid; p < n_pairs; p += 1024) {
+    const int e = ids[p];
+    if (e < 0 || e >= E_total) {
+      bad = 1;
+    } else {
+      const int le = e - e_begin;
+      if (le >= 0 && le < E_loc) atomicAdd(&s_hist[le], 1);
+    }
+  }
+  bad = __syncthreads_or(bad);
+  const int cnt = tid < E_loc ? s_hist[tid] : 0;
+  const int off = block_excl_scan_1024(cnt, s_wsum);
+  if (tid < E_loc) {
+    counts[tid] = cnt;
+    offsets[tid] = off;
+    s_run[tid] = off;
+  }
+  if (tid == E_loc - 1) offsets[E_loc] = off + cnt;
+  if (tile_offsets) {
+    const int tiles = (cnt + tile_m - 1) / tile_m;
+    const int toff = block_excl_scan_1024(tiles, s_wsum);
+    if (tid < E_loc) tile_offsets[tid] = toff;
+    if (tid == E_loc - 1) tile_offsets[E_loc] = toff + tiles;
+  }
+  if (tid == 0) err[0] = bad;
+  for (int64_t c0 = 0; c0 < n_pairs; c0 += kSmallChunk) {
+    for (int i = tid; i < 16 * E_loc; i += 1024) s_wcnt[i / E_loc][i % E_loc] = 0;
+    __syncthreads();
+    const int64_t p = c0 + tid;
+    int le = -1;
+    if (p < n_pairs) {
+      const int e = ids[p] - e_begin;
+      if (e >= 0 && e < E_loc) le = e;
+    }
+    const bool local = le >= 0;
+    uint64_t remaining = __ballot(local);
+    uint64_t mine = 0;
+    while (remaining) {
+      const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+      const int lead_e = __shfl(le, leader, kWave);
+      const uint64_t m = __ballot(local && le == lead_e);
+      if (local && le == lead_e) mine = m;
+      remaining &= ~m;
+    }
+    const uint64_t lower = mine & lanemask_lt();
+    if (local && lower == 0) s_wcnt[wave][le] = __popcll(mine);
+    __syncthreads();
+    if (p < n_pairs) {
+      int pos = -1;
+      if (local) {
+        pos = s_run[le] + __popcll(lower);
+        for (int w = 0; w < wave; ++w) pos += s_wcnt[w][le];
+        perm[pos] = static_cast<int32_t>(p);
+      }
+      inv[p] = pos;
+    }
+    __syncthreads();
+    for (int e = tid; e < E_loc; e += 1024) {
+      int add = 0;
+      for (int w = 0; w < 16; ++w) add += s_wcnt[w][e];
+      s_run[e] += add;
+    }
+    __syncthreads();
+  }
+}
+
 // One wave per token; rows are moved as 16-byte chunks, kChunks per lane in
 // flight at a time.
 constexpr int kChunks = 4;
@@ -237,6 +328,21 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int64_t n_pairs = a.T * a.k;
   const int64_t nb = n_pair_blocks(a.T, a.k);
   DispWs w = carve(a.ws, nb, E_loc);
+  const int row_chunks = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
+  if (n_pairs <= kSmallMaxPairs && E_loc <= kSmallMaxELoc) {
+    hipLaunchKernelGGL(k_disp_small, dim3(1), dim3(1024), 0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc,
+                       a.tile_m > 0 ? a.tile_m : 1, a.counts, a.offsets, a.tile_m > 0 ? a.tile_offsets : nullptr,
+                       a.perm, a.inv, w.err);
+    DBOMOE_CHECK_LAUNCH();
+    if (nb == 0) return MOE_OK;
+    int64_t blocks = (a.T + 3) / 4;
+    if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
+    hipLaunchKernelGGL(k_disp_gather, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const u32x4_t*>(a.x), a.T, row_chunks, a.k, a.inv,
+                       static_cast<u32x4_t*>(a.x_perm));
+    DBOMOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
   if (nb > 0) {
     hipLaunchKernelGGL(k_disp_count, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a.ids, n_pairs,
                        a.E_total, a.e_begin, E_loc, w.block_hist, w.block_err);
@@ -252,7 +358,6 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_disp_rank, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a.ids, n_pairs, a.e_begin,
                      E_loc, w.block_hist, a.offsets, a.perm, a.inv);
   DBOMOE_CHECK_LAUNCH();
-  const int row_chunks = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
   int64_t blocks = (a.T + 3) / 4;
   if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
   hipLaunchKernelGGL(k_disp_gather, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,

@@ -117,8 +117,12 @@ def test_dispatch(cid, small):
         assert C.binding.moe_get_device_error(g["ws"]) == 0
 
 
+# Up to 8192 pairs and 256 local experts the dispatch runs its one-workgroup
+# count/scan/rank kernel (pairs taken 1024 at a time); beyond, four kernels.
 @pytest.mark.parametrize("T,k,E,lo,hi", [(1, 1, 1, 0, 1), (3, 2, 5, 1, 4), (300, 8, 256, 0, 32),
-                                         (257, 6, 64, 0, 64), (64, 16, 300, 100, 300)])
+                                         (257, 6, 64, 0, 64), (64, 16, 300, 100, 300),
+                                         (1024, 8, 64, 0, 64), (1025, 8, 64, 0, 64),
+                                         (2048, 4, 256, 0, 256), (1000, 3, 300, 0, 257)])
 def test_dispatch_shapes(T, k, E, lo, hi):
     C = _gpu()
     rng = np.random.default_rng(T * 31 + k)
