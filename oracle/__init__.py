@@ -29,6 +29,8 @@ from .numerics import fp8_e4m3fn_value, FP8_E4M3FN_TABLE, decode, dequant_fp8_bl
 from .routing import router_logits, softmax_rows, sigmoid, select_topk, select_grouped, route
 from .dispatch import dispatch_ref
 from .ffn import silu, swiglu_expert, grouped_ffn_ref
+from .quant import (fp8_e4m3fn_encode, group_exponent, quant_rows_fp8, dequant_rows_fp8,
+                    fp8_roundtrip_rows, swiglu_expert_fp8act, grouped_ffn_fp8act_ref)
 from .layer import (split_point, expert_weights, shared_weights, moe_layer_token,
                     moe_layer_expert, moe_layer_microbatched, combine_ref, slice_view)
 
@@ -36,6 +38,8 @@ __all__ = [
     "fp8_e4m3fn_value", "FP8_E4M3FN_TABLE", "decode", "dequant_fp8_blocks",
     "router_logits", "softmax_rows", "sigmoid", "select_topk", "select_grouped", "route",
     "dispatch_ref", "silu", "swiglu_expert", "grouped_ffn_ref",
+    "fp8_e4m3fn_encode", "group_exponent", "quant_rows_fp8", "dequant_rows_fp8",
+    "fp8_roundtrip_rows", "swiglu_expert_fp8act", "grouped_ffn_fp8act_ref",
     "split_point", "expert_weights", "shared_weights", "moe_layer_token", "moe_layer_expert",
     "moe_layer_microbatched", "combine_ref", "slice_view",
 ]

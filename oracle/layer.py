@@ -19,6 +19,14 @@ import numpy as np
 from .numerics import decode, dequant_fp8_blocks
 from .routing import router_logits, route_cfg
 from .ffn import swiglu_expert
+from .quant import swiglu_expert_fp8act
+
+
+def _routed_expert(ov: dict):
+    """The routed experts' FFN: bf16 activations, or fp8 activations when the
+    call asks for them (ov["fp8_act"]); the shared experts always keep the
+    activation dtype."""
+    return swiglu_expert_fp8act if ov.get("fp8_act") else swiglu_expert
 
 
 def split_point(T: int, min_tokens_to_split: int = 2, split_at: int = -1):
@@ -96,7 +104,7 @@ def moe_layer_token(ov: dict, tokens=None) -> dict:
                 if el not in cache:
                     cache[el] = expert_weights(ov, el)
                 w13, w2 = cache[el]
-                out[r] += float(w[t, j]) * swiglu_expert(x[t:t + 1], w13, w2)[0]
+                out[r] += float(w[t, j]) * _routed_expert(ov)(x[t:t + 1], w13, w2)[0]
         for w13, w2 in shared:
             out[r] += swiglu_expert(x[t:t + 1], w13, w2)[0]
     return dict(logits=logits, ids=ids, w=w, out=out, tokens=tokens)
@@ -120,7 +128,7 @@ def moe_layer_expert(ov: dict, tokens=None) -> dict:
         if rows.size == 0:
             continue
         w13, w2 = expert_weights(ov, el)
-        y, s = swiglu_expert(x[tokens[rows]], w13, w2, with_scale=True)
+        y, s = _routed_expert(ov)(x[tokens[rows]], w13, w2, with_scale=True)
         wr = w[tokens[rows], slots][:, None]
         np.add.at(out, rows, wr * y)
         np.add.at(scale, rows, np.abs(wr) * s)
