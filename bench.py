@@ -24,8 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 KERNEL_SOURCES = ["combine_dual_overlap_amd/csrc/gemm_mfma.h", "combine_dual_overlap_amd/csrc/gemm_wstream.h",
+                  "combine_dual_overlap_amd/csrc/gemm_fp8.h", "combine_dual_overlap_amd/csrc/fp8_act.h",
                   "combine_dual_overlap_amd/csrc/ffn.hip"]
 
 
@@ -60,13 +61,16 @@ def read_traffic(workload: str):
         return None
 
 
-def gateup_work(cfg, counts_per_mb, rows_per_mb):
-    """Algorithmic bytes and flops of one gate/up GEMM launch per microbatch:
+def gateup_work(cfg, counts_per_mb, rows_per_mb, fp8_act=False):
+    """Algorithmic bytes and flops of one gate/up GEMM step per microbatch:
     weights of every routed expert that received rows and of the shared
     experts (each read once), the dispatched rows and the microbatch's rows for
-    the shared experts (read once), the SwiGLU outputs h (written once)."""
+    the shared experts (read once), the SwiGLU outputs h (written once).  With
+    fp8 activations the routed rows and h are one byte per element plus one
+    scale byte per 128."""
     w_s = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
     a_s = 4 if cfg.act == "f32" else 2
+    r_s = 1 + 1 / 128 if fp8_act else a_s
     I_sh = cfg.n_shared * cfg.shared_I
     out = []
     for counts, T_mb in zip(counts_per_mb, rows_per_mb):
@@ -75,7 +79,7 @@ def gateup_work(cfg, counts_per_mb, rows_per_mb):
         wbytes = hit * 2 * cfg.I * cfg.H * w_s
         if cfg.wdt == "fp8":
             wbytes += hit * (2 * cfg.I // 128) * (cfg.H // 128) * 4
-        nbytes = wbytes + M * cfg.H * a_s + M * cfg.I * a_s
+        nbytes = wbytes + M * cfg.H * r_s + M * cfg.I * r_s
         flops = 2.0 * M * cfg.H * 2 * cfg.I
         if I_sh:
             nbytes += 2 * I_sh * cfg.H * a_s + T_mb * cfg.H * a_s + T_mb * I_sh * a_s
@@ -96,7 +100,7 @@ def shared_slabs(cfg) -> int:
     return 1
 
 
-def comm_work(cfg, L, halves, comm_ms):
+def comm_work(cfg, L, halves, comm_ms, fp8_act=False):
     """Achieved HBM bandwidth of the dispatch step (count, scan, rank, gather)
     and of the combine, from their algorithmic bytes per microbatch: dispatch
     reads every token row with a local expert once and writes its dispatched
@@ -104,13 +108,14 @@ def comm_work(cfg, L, halves, comm_ms):
     shared slabs, ids and weights, and writes every token row."""
     import torch
     s = 4 if cfg.act == "f32" else 2
+    s_out = 1 + 1 / 128 if fp8_act else s         # dispatched row: codes + scale bytes
     d_bytes, c_bytes = [], []
     for mb, (a, b) in enumerate(halves):
         n = b - a
         inv = L.view(mb, "inv", torch.int32, (n * cfg.k,), T=cfg.T).cpu().numpy().reshape(n, cfg.k)
         M = int((inv >= 0).sum())
         t_hit = int((inv >= 0).any(axis=1).sum())
-        d_bytes.append(t_hit * cfg.H * s + M * cfg.H * s + 4 * n * cfg.k + 4 * M + 4 * n * cfg.k)
+        d_bytes.append(t_hit * cfg.H * s + M * cfg.H * s_out + 4 * n * cfg.k + 4 * M + 4 * n * cfg.k)
         c_bytes.append(M * cfg.H * s + 8 * n * cfg.k + n * cfg.H * s + shared_slabs(cfg) * n * cfg.H * s)
     out = {"schedule": "serial"}
     for name, cols, byts in (("dispatch", [0, 1], d_bytes), ("combine", [2, 3], c_bytes)):
@@ -122,7 +127,7 @@ def comm_work(cfg, L, halves, comm_ms):
     return out
 
 
-def cpu_baseline(inp, cfg, budget_s: float):
+def cpu_baseline(inp, cfg, budget_s: float, fp8_act=False):
     """The oracle (as it stands) on a bounded sample of the same workload:
     its first tokens (all of them when one run fits the budget)."""
     import oracle as O
@@ -132,7 +137,7 @@ def cpu_baseline(inp, cfg, budget_s: float):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    ov = W.oracle_view(inp)
+    ov = dict(W.oracle_view(inp), fp8_act=fp8_act)
     n = cfg.T if cfg.T <= 512 else 512
     sub = O.slice_view(ov, 0, n)
     t0 = time.perf_counter()
@@ -158,6 +163,8 @@ def main():
     ap.add_argument("--comm-cu-budget", type=int, default=0)
     ap.add_argument("--ffn-tile-m", type=int, default=0,
                     help="expert FFN row tile: 0 automatic, 16 weight-streaming kernel, 32/64/128 LDS-tiled kernel")
+    ap.add_argument("--fp8-act", action="store_true",
+                    help="routed experts with fp8 activations (fp8-weight configurations 3 and 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -188,7 +195,10 @@ def main():
     cfg = W.get_config(args.config)
     log(f"bench: generating {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I}")
     inp = W.make_inputs(cfg)
-    L = DeviceLayer(inp, device="cuda:0")
+    if args.fp8_act and cfg.wdt != "fp8":
+        print("--fp8-act needs fp8 weights (configurations 3 and 4)", file=sys.stderr)
+        sys.exit(2)
+    L = DeviceLayer(inp, device="cuda:0", fp8_act=args.fp8_act)
     K, Wm = args.steps, args.warmup
     T = cfg.T
 
@@ -260,14 +270,14 @@ def main():
     T0 = L.ctx.last_stats()["T0"]
     halves = [(0, T0), (T0, T)] if T0 < T else [(0, T)]
     counts = [L.view(mb, "counts", torch.int32, (cfg.E_loc,), T=T).cpu().numpy() for mb in range(len(halves))]
-    work = gateup_work(cfg, counts, [b - a for a, b in halves])
+    work = gateup_work(cfg, counts, [b - a for a, b in halves], args.fp8_act)
     bytes_launch = float(np.mean([w[0] for w in work]))
     flops_launch = float(np.mean([w[1] for w in work]))
     avg_s = float(np.mean(gu_ms)) / 1e3
     ai = flops_launch / bytes_launch
-    mfma_peak = MFMA_PEAK_TFLOPS["f32" if cfg.act == "f32" else "bf16"]
+    mfma_peak = MFMA_PEAK_TFLOPS["f32" if cfg.act == "f32" else "fp8" if args.fp8_act else "bf16"]
     hbm_bound = ai < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
-    traffic = read_traffic(f"c{args.config}")
+    traffic = read_traffic(f"c{args.config}" + ("_fp8act" if args.fp8_act else ""))
     if hbm_bound:
         achieved = bytes_launch / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -281,25 +291,28 @@ def main():
     I_sh = cfg.n_shared * cfg.shared_I
     tile = args.ffn_tile_m or B.moe_ffn_auto_tile(B.dtype_code(L.x), B.dtype_code(L.w13), cfg.H, cfg.I,
                                                   -(-T_mb0 * cfg.k // cfg.E), T_mb0 if I_sh else 0, I_sh)
+    if args.fp8_act:
+        tile = 128 if tile >= 128 else 64
     kname = ("k_gemm_nt_f32 (fp32 SIMT)" if cfg.act == "f32" else
+             f"k_gemm_f8 ({tile}-row LDS tiles, fp8 x fp8)" if args.fp8_act else
              "k_gemm_ws (weight-streaming, 16-row tiles)" if tile == 16 else f"k_gemm_nt ({tile}-row LDS tiles)")
     roof["kernel"] = f"gate/up expert GEMM + SwiGLU, routed and shared experts: {kname}, MODE_GATEUP"
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
     roof["algorithmic_bytes_per_launch"] = int(bytes_launch)
     roof["algorithmic_flops_per_launch"] = int(flops_launch)
 
-    comm_rec = comm_work(cfg, L, halves, comm)
+    comm_rec = comm_work(cfg, L, halves, comm, args.fp8_act)
 
     base = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
-        base = cpu_baseline(inp, cfg, args.cpu_budget_s)
+        base = cpu_baseline(inp, cfg, args.cpu_budget_s, args.fp8_act)
 
     # The headline is the DBO step replayed from a HIP graph (how a decode
     # layer is deployed: the whole step, both streams and their events, one
     # launch); eager numbers sit beside it.
     value = T * K / dt_graph
-    dtype = {"f32": "f32", "bf16": "bf16"}[cfg.act]
+    dtype = "fp8" if args.fp8_act else {"f32": "f32", "bf16": "bf16"}[cfg.act]
     rec = {
         "metric": "MoE-layer tokens/sec (DBO vs serial) + MFMA util % and HBM GB/s % of peak",
         "value": round(value, 1),
@@ -315,7 +328,8 @@ def main():
         "data": "synthetic (seeded random activations and weights of the layer's shape)",
         "config": {"workload": cfg.name, "T": T, "split": [T0, T - T0] if T0 < T else [T], "H": cfg.H,
                    "E": cfg.E, "E_local": cfg.E_loc, "k": cfg.k, "I": cfg.I, "shared_experts": cfg.n_shared,
-                   "weights": cfg.wdt, "schedule": args.schedule, "comm_cu_budget": args.comm_cu_budget,
+                   "weights": cfg.wdt, "expert_activations": "fp8" if args.fp8_act else cfg.act,
+                   "schedule": args.schedule, "comm_cu_budget": args.comm_cu_budget,
                    "execution": "HIP graph replay of one dbo_moe_layer call per step"},
         "eager_tokens_per_s": round(T * K / dt, 1),
         "serial_graph_tokens_per_s": round(T * K / dt_serial_graph, 1),

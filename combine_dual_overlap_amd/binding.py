@@ -28,6 +28,7 @@ EXPORTED = [
     "dbo_ctx_create", "dbo_ctx_destroy", "dbo_ctx_set_timing", "dbo_ctx_ffn_times", "dbo_ctx_comm_times",
     "dbo_ctx_last_stats",
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "dbo_moe_layer", "moe_status_string",
+    "moe_quant_fp8_rows", "moe_dispatch_fp8", "moe_ffn_fp8_workspace_size", "moe_grouped_ffn_fp8",
 ]
 
 
@@ -45,7 +46,7 @@ class moe_layer_desc(ctypes.Structure):
                 ("w_router", ctypes.c_void_p), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
                 ("shared_I", ctypes.c_int32), ("shared_w13", ctypes.c_void_p),
-                ("shared_w2", ctypes.c_void_p)]
+                ("shared_w2", ctypes.c_void_p), ("fp8_act", ctypes.c_int32)]
 
 
 class dbo_opts(ctypes.Structure):
@@ -97,6 +98,12 @@ def lib():
             "dbo_moe_layer": (_i32, [_vp, ctypes.POINTER(moe_layer_desc), _vp, _i64, _vp, _vp, _vp,
                                      ctypes.POINTER(dbo_opts), _vp, _sz, _vp, _vp]),
             "moe_status_string": (ctypes.c_char_p, [_i32]),
+            "moe_quant_fp8_rows": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
+            "moe_dispatch_fp8": (_i32, [_vp, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+            "moe_ffn_fp8_workspace_size": (_sz, [_i64, _i32]),
+            "moe_grouped_ffn_fp8": (_i32, [_vp, _vp, _i32, _i32, _vp, _i32, _i64, _vp, _vp, _vp, _vp,
+                                           _vp, _i32, _vp, _sz, _vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -200,6 +207,35 @@ def moe_grouped_ffn(x_perm, I, offsets, E_loc, w13, w2, y_perm, ws, w13_scale=No
                                  ptr(w2), dtype_code(w13), ptr(w13_scale), ptr(w2_scale), ptr(y_perm), tile_m,
                                  ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)),
            "moe_grouped_ffn")
+
+
+def moe_quant_fp8_rows(x, q, scale, stream=None):
+    n, K = x.shape
+    _check(lib().moe_quant_fp8_rows(ptr(x), n, K, ptr(q), ptr(scale), stream_handle(stream)), "moe_quant_fp8_rows")
+
+
+def moe_dispatch_fp8(x, topk_ids, E_total, expert_begin, expert_end, counts, offsets, perm, inv, xq_perm,
+                     xq_scale, ws, tile_m=0, tile_offsets=None, stream=None):
+    T, H = x.shape
+    k = topk_ids.shape[1] if topk_ids.dim() == 2 else 1
+    _check(lib().moe_dispatch_fp8(ptr(x), T, H, ptr(topk_ids), k, E_total, expert_begin, expert_end, tile_m,
+                                  ptr(counts), ptr(offsets), ptr(tile_offsets), ptr(perm), ptr(inv), ptr(xq_perm),
+                                  ptr(xq_scale), ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)),
+           "moe_dispatch_fp8")
+
+
+def moe_ffn_fp8_workspace_size(cap_rows: int, I: int) -> int:
+    return lib().moe_ffn_fp8_workspace_size(cap_rows, I)
+
+
+def moe_grouped_ffn_fp8(xq_perm, xq_scale, I, offsets, E_loc, w13, w2, w13_scale, w2_scale, y_perm, ws,
+                        tile_m=0, cap_rows=None, stream=None):
+    cap = xq_perm.shape[0] if cap_rows is None else cap_rows
+    H = xq_perm.shape[1]
+    _check(lib().moe_grouped_ffn_fp8(ptr(xq_perm), ptr(xq_scale), H, I, ptr(offsets), E_loc, cap, ptr(w13),
+                                     ptr(w2), ptr(w13_scale), ptr(w2_scale), ptr(y_perm), tile_m, ptr(ws),
+                                     ws.numel() * ws.element_size(), stream_handle(stream)),
+           "moe_grouped_ffn_fp8")
 
 
 def moe_combine(y_perm, T, k, inv, topk_w, out, shared_out=None, stream=None):

@@ -109,6 +109,7 @@ struct DispatchArgs {
   const int32_t* ids; int32_t k; int32_t E_total; int32_t e_begin; int32_t e_end; int32_t tile_m;
   int32_t* counts; int32_t* offsets; int32_t* tile_offsets; int32_t* perm; int32_t* inv;
   void* x_perm; void* ws; int32_t max_blocks;
+  uint8_t* x_scale;        // non-NULL: x_perm receives fp8 codes and x_scale the E8M0 bytes [rows][H/128]
 };
 size_t dispatch_ws_bytes(int64_t T, int32_t k, int32_t E_loc);
 moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s);
@@ -123,8 +124,14 @@ struct FfnArgs {
   // experts): rows1 rows of x1, intermediate size I1, weights in the activation
   // dtype, output y1 [rows1, H], intermediate h1 [rows1, I1].
   const void* x1; int64_t rows1; int32_t I1; const void* w13_1; const void* w2_1; void* y1; void* h1;
+  // fp8 activations: x holds E4M3 codes and xs their E8M0 bytes [cap_rows][H/128];
+  // the routed experts then run fp8 x fp8 MFMAs and h (in `h`, see
+  // ffn_fp8_ws_bytes) is quantised the same way.  NULL: x is in act.
+  const uint8_t* xs;
 };
 moe_status launch_ffn(const FfnArgs& a, hipStream_t s);
+moe_status check_ffn_fp8_shapes(int32_t H, int32_t I, int32_t E_loc, const float* s13, const float* s2);
+size_t ffn_fp8_ws_bytes(int64_t cap_rows, int32_t I);
 moe_status check_ffn_shapes(moe_dtype act, moe_dtype wdt, int32_t H, int32_t I, int32_t E_loc,
                             const float* s13, const float* s2);
 // K chunks of a dense (shared) expert's down projection run in the grouped

@@ -20,8 +20,10 @@
 //               an LDS prefix over the 4 waves; writes perm and inv.
 //  4. gather  - one wave per token: the row is read from HBM once (16-byte
 //               vector loads, several in flight per lane) and written to each of
-//               its k destination rows.
-#include "common.h"
+//               its k destination rows.  The fp8 variant quantises the row on
+//               the way (groups of 128 columns, E8M0 scales; fp8_act.h) and
+//               writes codes and scale bytes instead.
+#include "fp8_act.h"
 
 namespace dbomoe {
 
@@ -323,25 +325,90 @@ __global__ __launch_bounds__(256) void k_disp_gather(const u32x4_t* __restrict__
   }
 }
 
+// fp8 gather: 8 bf16 per lane per 16-byte load, so a 128-column group is 16
+// adjacent lanes; their amax is combined with four xor shuffles.  inv == NULL
+// maps row t to row t (plain row quantisation, k = 1).
+__global__ __launch_bounds__(256) void k_disp_gather_q8(const u32x4_t* __restrict__ x, int64_t T, int row_chunks,
+                                                        int k, const int32_t* __restrict__ inv,
+                                                        uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t H = static_cast<int64_t>(row_chunks) * 8;
+  const int groups = row_chunks / 16;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave; t < T; t += stride) {
+    const u32x4_t* src = x + t * row_chunks;
+    for (int c0 = 0; c0 < row_chunks; c0 += 64 * kChunks) {
+      u32x4_t v[kChunks];
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        const int c = c0 + i * 64 + lane;
+        v[i] = c < row_chunks ? src[c] : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      uint32_t q[kChunks][2], sb[kChunks];
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) {
+        float f[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          f[2 * w] = __uint_as_float(v[i][w] << 16);
+          f[2 * w + 1] = __uint_as_float(v[i][w] & 0xffff0000u);
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+        sb[i] = e8m0_for_amax(m);
+        const float is = e8m0_inv_scale(sb[i]);
+        q[i][0] = fp8x4_rne(f[0] * is, f[1] * is, f[2] * is, f[3] * is);
+        q[i][1] = fp8x4_rne(f[4] * is, f[5] * is, f[6] * is, f[7] * is);
+      }
+      for (int j = 0; j < k; ++j) {
+        const int64_t pos = inv ? inv[t * k + j] : t;
+        if (pos < 0) continue;
+        uint8_t* dst = xq + pos * H;
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+          const int c = c0 + i * 64 + lane;
+          if (c < row_chunks) {
+            *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(q[i][0], q[i][1]);
+            if ((lane & 15) == 0) xs[pos * groups + c / 16] = static_cast<uint8_t>(sb[i]);
+          }
+        }
+      }
+    }
+  }
+}
+
+static moe_status launch_gather(const DispatchArgs& a, hipStream_t s) {
+  int64_t blocks = (a.T + 3) / 4;
+  if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
+  const int row_chunks = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
+  if (a.x_scale) {
+    hipLaunchKernelGGL(k_disp_gather_q8, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const u32x4_t*>(a.x), a.T, row_chunks, a.k, a.inv,
+                       static_cast<uint8_t*>(a.x_perm), a.x_scale);
+  } else {
+    hipLaunchKernelGGL(k_disp_gather, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const u32x4_t*>(a.x), a.T, row_chunks, a.k, a.inv,
+                       static_cast<u32x4_t*>(a.x_perm));
+  }
+  DBOMOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
 moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int E_loc = a.e_end - a.e_begin;
   const int64_t n_pairs = a.T * a.k;
   const int64_t nb = n_pair_blocks(a.T, a.k);
   DispWs w = carve(a.ws, nb, E_loc);
-  const int row_chunks = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
   if (n_pairs <= kSmallMaxPairs && E_loc <= kSmallMaxELoc) {
     hipLaunchKernelGGL(k_disp_small, dim3(1), dim3(1024), 0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc,
                        a.tile_m > 0 ? a.tile_m : 1, a.counts, a.offsets, a.tile_m > 0 ? a.tile_offsets : nullptr,
                        a.perm, a.inv, w.err);
     DBOMOE_CHECK_LAUNCH();
     if (nb == 0) return MOE_OK;
-    int64_t blocks = (a.T + 3) / 4;
-    if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
-    hipLaunchKernelGGL(k_disp_gather, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                       static_cast<const u32x4_t*>(a.x), a.T, row_chunks, a.k, a.inv,
-                       static_cast<u32x4_t*>(a.x_perm));
-    DBOMOE_CHECK_LAUNCH();
-    return MOE_OK;
+    return launch_gather(a, s);
   }
   if (nb > 0) {
     hipLaunchKernelGGL(k_disp_count, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a.ids, n_pairs,
@@ -358,13 +425,7 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_disp_rank, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a.ids, n_pairs, a.e_begin,
                      E_loc, w.block_hist, a.offsets, a.perm, a.inv);
   DBOMOE_CHECK_LAUNCH();
-  int64_t blocks = (a.T + 3) / 4;
-  if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
-  hipLaunchKernelGGL(k_disp_gather, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                     static_cast<const u32x4_t*>(a.x), a.T, row_chunks, a.k, a.inv,
-                     static_cast<u32x4_t*>(a.x_perm));
-  DBOMOE_CHECK_LAUNCH();
-  return MOE_OK;
+  return launch_gather(a, s);
 }
 
 }  // namespace dbomoe
@@ -398,8 +459,54 @@ extern "C" moe_status moe_dispatch(const void* x, moe_dtype act, int64_t T, int3
   if (T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (ws_bytes < dispatch_ws_bytes(T, k, E_loc)) return MOE_ERR_WORKSPACE;
   DispatchArgs a{x, act, T, H, topk_ids, k, E_total, expert_begin, expert_end, tile_m,
-                 counts, offsets, tile_offsets, perm, inv, x_perm, ws, 0};
+                 counts, offsets, tile_offsets, perm, inv, x_perm, ws, 0, nullptr};
   return launch_dispatch(a, as_stream(stream));
+}
+
+extern "C" moe_status moe_dispatch_fp8(const void* x, int64_t T, int32_t H, const int32_t* topk_ids, int32_t k,
+                                       int32_t E_total, int32_t expert_begin, int32_t expert_end, int32_t tile_m,
+                                       int32_t* counts, int32_t* offsets, int32_t* tile_offsets, int32_t* perm,
+                                       int32_t* inv, uint8_t* xq_perm, uint8_t* xq_scale, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  if (H <= 0 || H % kQGroup) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && !xq_scale) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && !aligned16(xq_scale)) return MOE_ERR_MISALIGNED;
+  // the bf16 checks cover everything else (x_perm alignment, ranges, workspace)
+  if (T < 0 || k < 1 || k > 16 || E_total < 1) return MOE_ERR_INVALID_ARG;
+  if (expert_begin < 0 || expert_end <= expert_begin || expert_end > E_total) return MOE_ERR_INVALID_ARG;
+  const int E_loc = expert_end - expert_begin;
+  if (E_loc > kMaxELoc) return MOE_ERR_UNSUPPORTED;
+  if (tile_offsets && tile_m <= 0) return MOE_ERR_INVALID_ARG;
+  if (!counts || !offsets || !ws) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !topk_ids || !perm || !inv || !xq_perm)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(counts) || !aligned16(offsets) ||
+      (tile_offsets && !aligned16(tile_offsets)) || !aligned16(perm) || !aligned16(inv) ||
+      !aligned16(xq_perm) || !aligned256(ws))
+    return MOE_ERR_MISALIGNED;
+  if (T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < dispatch_ws_bytes(T, k, E_loc)) return MOE_ERR_WORKSPACE;
+  DispatchArgs a{x, MOE_BF16, T, H, topk_ids, k, E_total, expert_begin, expert_end, tile_m,
+                 counts, offsets, tile_offsets, perm, inv, xq_perm, ws, 0, xq_scale};
+  return launch_dispatch(a, as_stream(stream));
+}
+
+extern "C" moe_status moe_quant_fp8_rows(const void* x, int64_t n, int32_t K, uint8_t* q, uint8_t* scale,
+                                         void* stream) {
+  if (n < 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+  if (K % kQGroup) return MOE_ERR_UNSUPPORTED;
+  if (n == 0) return MOE_OK;
+  if (!x || !q || !scale) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return MOE_ERR_MISALIGNED;
+  DispatchArgs a{};
+  a.x = x;
+  a.act = MOE_BF16;
+  a.T = n;
+  a.H = K;
+  a.k = 1;
+  a.inv = nullptr;
+  a.x_perm = q;
+  a.x_scale = scale;
+  return launch_gather(a, as_stream(stream));
 }
 
 extern "C" moe_status moe_get_device_error(const void* dispatch_ws, int32_t* code, void* stream) {

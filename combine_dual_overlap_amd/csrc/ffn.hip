@@ -4,9 +4,13 @@
 // The expert compute of "[Core/DBO][1/N] Add Dual-Batch Overlap mechanism to
 // VLLM" (performance discussion: batched MoE GEMM + act-and-mul).  Reading:
 // W13 = [gate rows 0..I) ; up rows I..2I)], h = silu(gate) * up rounded to the
-// activation dtype, y = h W2^T.
+// activation dtype, y = h W2^T.  With fp8 activations (the fused SiLU-mul +
+// fp8 quantisation op of the same page, CI discussion) the rows arrive as E4M3
+// codes with per-128-column E8M0 scales and h is quantised the same way
+// (gemm_fp8.h, fp8_act.h).
 #include <cmath>
 
+#include "gemm_fp8.h"
 #include "gemm_wstream.h"
 
 namespace dbomoe {
@@ -127,8 +131,102 @@ bool ffn_ws_fits(moe_dtype act, int32_t H, int32_t I, int64_t rows1, int32_t I1)
   return true;
 }
 
+// ---- fp8 activations ------------------------------------------------------
+
+size_t ffn_fp8_ws_bytes(int64_t cap_rows, int32_t I) {
+  return align_up(static_cast<size_t>(cap_rows) * I, 256) + align_up(static_cast<size_t>(cap_rows) * (I / kQGroup), 256);
+}
+
+moe_status check_ffn_fp8_shapes(int32_t H, int32_t I, int32_t E_loc, const float* s13, const float* s2) {
+  if (H <= 0 || I <= 0 || E_loc < 1) return MOE_ERR_INVALID_ARG;
+  if (E_loc > 256) return MOE_ERR_UNSUPPORTED;
+  if (H % kF8BN || I % kQGroup) return MOE_ERR_UNSUPPORTED;
+  if (!s13 || !s2) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// Row tile of the fp8 kernel: 64 or 128 (8 waves; 64 rows is its smallest tile).
+static int f8_tile_m(int tile_m, int64_t rows_hint) {
+  const int bm = tile_m > 0 ? tile_m : choose_tile_m(rows_hint);
+  return bm >= 128 ? 128 : 64;
+}
+
+template <int MODE>
+static void launch_f8(int bm, dim3 grid, hipStream_t s, const F8Params& p) {
+  if (bm == 128)
+    hipLaunchKernelGGL((k_gemm_f8<128, MODE>), grid, dim3(kF8Threads), 0, s, p);
+  else
+    hipLaunchKernelGGL((k_gemm_f8<64, MODE>), grid, dim3(kF8Threads), 0, s, p);
+}
+
+// Routed experts through the fp8 kernel; the shared experts (weights in the
+// activation dtype) through the bf16 kernel as a dense group of their own.
+static moe_status launch_ffn_fp8(const FfnArgs& a, hipStream_t s) {
+  const bool dense = a.offsets == nullptr;
+  const int bm = f8_tile_m(a.tile_m, a.rows_hint);
+  uint8_t* hq = static_cast<uint8_t*>(a.h);
+  uint8_t* hs = hq + align_up(static_cast<size_t>(a.cap_rows) * a.I, 256);
+  F8Params p1{};
+  p1.loc.offsets = a.offsets;
+  p1.loc.E_loc = a.E_loc;
+  p1.loc.dense_rows = a.cap_rows;
+  p1.loc.g[0].n_tiles = a.I / (kF8BN / 2);
+  p1.g = F8Group{static_cast<const uint8_t*>(a.x), a.xs, static_cast<const uint8_t*>(a.w13), a.s13,
+                 a.H, a.I, 2 * a.I, hq, hs};
+  F8Params p2 = p1;
+  p2.loc.g[0].n_tiles = a.H / kF8BN;
+  p2.g = F8Group{hq, hs, static_cast<const uint8_t*>(a.w2), a.s2, a.I, a.H, a.H, a.y, nullptr};
+  const dim3 grid1(static_cast<unsigned>(gemm_grid(tiles_max(bm, a.cap_rows, a.E_loc, dense, p1.loc.g[0].n_tiles, 0, 0, 0))));
+  const dim3 grid2(static_cast<unsigned>(gemm_grid(tiles_max(bm, a.cap_rows, a.E_loc, dense, p2.loc.g[0].n_tiles, 0, 0, 0))));
+
+  // shared experts: group 1 only (group 0 keeps no tiles)
+  GemmParams q1{}, q2{};
+  int bm_sh = 0;
+  dim3 gs1, gs2;
+  if (a.rows1 > 0) {
+    bm_sh = choose_tile_m(a.rows1);
+    q1.rows1 = a.rows1;
+    q1.E1 = 1;
+    q1.g[1] = gate_up_group(a.x1, a.H, a.I1, a.w13_1, nullptr, a.h1);
+    q2 = q1;
+    const int n_ch = dense_down_chunks(MOE_BF16, a.I1, a.I);
+    const int Kc = a.I1 / n_ch;
+    GemmGroup gd = down_group(a.h1, a.H, a.I1, a.w2_1, nullptr, a.y1);
+    gd.K = Kc;
+    gd.a_estride = Kc;
+    gd.b_estride = Kc;
+    gd.c_estride = a.rows1 * a.H;
+    q2.g[1] = gd;
+    q2.E1 = n_ch;
+    gs1 = dim3(static_cast<unsigned>(gemm_grid(tiles_max(bm_sh, 0, 1, true, 0, a.rows1, q1.E1, q1.g[1].n_tiles))));
+    gs2 = dim3(static_cast<unsigned>(gemm_grid(tiles_max(bm_sh, 0, 1, true, 0, a.rows1, q2.E1, q2.g[1].n_tiles))));
+  }
+
+  if (a.t0 && hipEventRecord(a.t0, s) != hipSuccess) return MOE_ERR_HIP;
+  if (a.cap_rows > 0) {
+    launch_f8<MODE_GATEUP>(bm, grid1, s, p1);
+    DBOMOE_CHECK_LAUNCH();
+  }
+  if (a.rows1 > 0) {
+    launch_mfma<MODE_GATEUP, false>(bm_sh, gs1, s, q1);
+    DBOMOE_CHECK_LAUNCH();
+  }
+  if (a.t1 && hipEventRecord(a.t1, s) != hipSuccess) return MOE_ERR_HIP;
+  if (a.cap_rows > 0) {
+    launch_f8<MODE_DOWN>(bm, grid2, s, p2);
+    DBOMOE_CHECK_LAUNCH();
+  }
+  if (a.rows1 > 0) {
+    launch_mfma<MODE_DOWN, false>(bm_sh, gs2, s, q2);
+    DBOMOE_CHECK_LAUNCH();
+  }
+  if (a.t2 && hipEventRecord(a.t2, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.cap_rows == 0 && a.rows1 == 0) return MOE_OK;
+  if (a.xs) return launch_ffn_fp8(a, s);
   if (a.act == MOE_F32) return launch_ffn_f32(a, s);
   const bool fp8 = a.wdt == MOE_FP8_E4M3FN;
   const bool dense = a.offsets == nullptr;
@@ -226,6 +324,49 @@ extern "C" int32_t moe_ffn_auto_tile(moe_dtype act, moe_dtype wdt, int32_t H, in
 extern "C" size_t moe_ffn_workspace_size(int64_t cap_rows, int32_t I, moe_dtype act) {
   if (cap_rows < 0 || I <= 0 || (act != MOE_F32 && act != MOE_BF16)) return 0;
   return ffn_ws_bytes(cap_rows, I, act);
+}
+
+extern "C" size_t moe_ffn_fp8_workspace_size(int64_t cap_rows, int32_t I) {
+  if (cap_rows < 0 || I <= 0 || I % kQGroup) return 0;
+  return ffn_fp8_ws_bytes(cap_rows, I);
+}
+
+extern "C" moe_status moe_grouped_ffn_fp8(const uint8_t* xq_perm, const uint8_t* xq_scale, int32_t H, int32_t I,
+                                          const int32_t* offsets, int32_t E_loc, int64_t cap_rows,
+                                          const uint8_t* w13, const uint8_t* w2, const float* w13_scale,
+                                          const float* w2_scale, void* y_perm, int32_t tile_m, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  moe_status st = check_ffn_fp8_shapes(H, I, E_loc, w13_scale, w2_scale);
+  if (st != MOE_OK) return st;
+  if (cap_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (!offsets && E_loc != 1) return MOE_ERR_INVALID_ARG;
+  if (tile_m != 0 && tile_m != 64 && tile_m != 128) return MOE_ERR_UNSUPPORTED;
+  if (cap_rows == 0) return MOE_OK;
+  if (cap_rows > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!xq_perm || !xq_scale || !w13 || !w2 || !y_perm || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(xq_perm) || !aligned16(xq_scale) || !aligned16(w13) || !aligned16(w2) || !aligned16(y_perm) ||
+      (offsets && !aligned16(offsets)) || !aligned16(w13_scale) || !aligned16(w2_scale) || !aligned256(ws))
+    return MOE_ERR_MISALIGNED;
+  if (ws_bytes < ffn_fp8_ws_bytes(cap_rows, I)) return MOE_ERR_WORKSPACE;
+  FfnArgs a{};
+  a.x = xq_perm;
+  a.xs = xq_scale;
+  a.act = MOE_BF16;
+  a.H = H;
+  a.I = I;
+  a.offsets = offsets;
+  a.E_loc = E_loc;
+  a.cap_rows = cap_rows;
+  a.rows_hint = offsets ? cap_rows / E_loc : cap_rows;
+  a.w13 = w13;
+  a.w2 = w2;
+  a.wdt = MOE_FP8_E4M3FN;
+  a.s13 = w13_scale;
+  a.s2 = w2_scale;
+  a.y = y_perm;
+  a.tile_m = tile_m;
+  a.h = ws;
+  return launch_ffn(a, as_stream(stream));
 }
 
 extern "C" moe_status moe_grouped_ffn(const void* x_perm, moe_dtype act, int32_t H, int32_t I,

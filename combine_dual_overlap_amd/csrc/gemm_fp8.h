@@ -1,0 +1,343 @@
+// fp8 x fp8 grouped expert GEMM for gfx950 (activations and weights E4M3 fn).
+//
+// The fp8 expert path that the fused SiLU-mul + fp8 quantisation op of
+// "[Core/DBO][1/N] Add Dual-Batch Overlap mechanism to VLLM" (CI discussion)
+// feeds.  C[m, n] = sum_k A[m, k] B[n, k] with
+//   A = activation codes times the row's per-128-column power-of-two scale,
+//   B = weight codes times the weight's 128 x 128 block scale (fp32).
+//
+// Work decomposition (the tile map is the one of the bf16 kernel,
+// locate_tile: device-side per-expert row counts, XCD-aware order)
+//  * BM activation rows x 256 weight rows per workgroup, 8 waves.  For the
+//    gate/up GEMM a tile holds 128 gate rows and the 128 matching up rows, so
+//    the tile owns whole 128-column groups of h and can quantise h in its
+//    epilogue (per-row amax over the tile's 128 h columns, exchanged in LDS).
+//  * K advances 128 per stage: one E4M3 K block of 128 bytes per row, the
+//    same LDS geometry as a 64-wide bf16 stage (16-byte chunks XOR-swizzled by
+//    row), half the LDS bytes per flop.  Two-deep register ring of global loads,
+//    double-buffered LDS, one barrier per stage, unconditional steady-state
+//    loads (the last stages are peeled).
+//  * One v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 tile per stage.  The
+//    hardware applies the activation row's E8M0 byte (scale operand of A; the
+//    B scale byte is 127 = 1.0).  The weight block scale changes with the K
+//    block, so each stage's product is accumulated into fp32 as
+//    acc += scale_w * p (promotion per K block).
+//  * Operand lanes: lane l holds row (or weight row) l % 16 and the 32 bytes
+//    [32 (l / 16), 32 (l / 16) + 32) of the stage's K block.  A and B use the
+//    same K assignment, so every product pairs matching K indices.
+#pragma once
+
+#include "fp8_act.h"
+#include "gemm_mfma.h"
+
+namespace dbomoe {
+
+constexpr int kF8BK = 128;          // K per stage (= bytes per row per stage)
+constexpr int kF8BN = 256;          // weight rows per column tile
+constexpr int kF8Threads = 512;     // 8 waves
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// Byte offset of 16-byte chunk c of LDS row r (rows of 128 bytes).
+__device__ __forceinline__ int lds8_off(int r, int c) { return r * kF8BK + ((c ^ (r & 7)) << 4); }
+
+struct F8Group {
+  const uint8_t* A;       // activation codes [rows][K]
+  const uint8_t* As;      // E8M0 bytes [rows][K / 128]
+  const uint8_t* B;       // weight codes [experts][b_rows][K]
+  const float* Bs;        // weight block scales [experts][b_rows / 128][K / 128]
+  int K;                  // multiple of 128
+  int N;                  // I (gate/up) or H (down)
+  int b_rows;             // 2I or H
+  void* C;                // gate/up: h codes [rows][N]; down: bf16 [rows][N]
+  uint8_t* Cs;            // gate/up: h E8M0 bytes [rows][N / 128]
+};
+
+struct F8Params {
+  GemmParams loc;         // tile map only: offsets, E_loc, dense_rows, g[0].n_tiles
+  F8Group g;
+};
+
+template <int BM>
+struct F8Shape {
+  static constexpr int WAVES_M = BM == 128 ? 2 : 1;
+  static constexpr int WAVES_N = 8 / WAVES_M;
+  static constexpr int WM = BM / WAVES_M;          // 64
+  static constexpr int WN = kF8BN / WAVES_N;       // 64 (BM 128) or 32 (BM 64)
+  static constexpr int TM = WM / 16;
+  static constexpr int TN = WN / 16;
+  static_assert(BM == 64 || BM == 128, "row tile");
+};
+
+// LDS row of the weight tile -> weight row inside the expert's matrix.
+template <int MODE>
+__device__ __forceinline__ int f8_b_row(const F8Group& g, int nt, int r) {
+  if constexpr (MODE == MODE_GATEUP)
+    return r < kF8BN / 2 ? nt * (kF8BN / 2) + r : g.N + nt * (kF8BN / 2) + (r - kF8BN / 2);
+  else
+    return nt * kF8BN + r;
+}
+
+// First LDS weight row of the wave's tn-th 16-column MFMA tile.
+template <int MODE, int WN, int TN>
+__device__ __forceinline__ int f8_b_lds_row(int wn, int tn) {
+  if constexpr (MODE == MODE_GATEUP)
+    return tn < TN / 2 ? wn * (WN / 2) + tn * 16 : kF8BN / 2 + wn * (WN / 2) + (tn - TN / 2) * 16;
+  else
+    return wn * WN + tn * 16;
+}
+
+template <int BM, int MODE>
+__device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t, uint8_t (*sA)[BM * kF8BK],
+                                             uint8_t (*sB)[kF8BN * kF8BK]) {
+  using S = F8Shape<BM>;
+  constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
+  constexpr int CA = BM * (kF8BK / 16) / kF8Threads;     // 16-byte A chunks per thread
+  constexpr int CB = kF8BN * (kF8BK / 16) / kF8Threads;  // 16-byte B chunks per thread
+  static_assert(CA >= 1 && CB >= 1, "chunking");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / S::WAVES_N;
+  const int wn = wave % S::WAVES_N;
+  const int K = g.K;
+  const int KT = K / kF8BK;
+  const int KB = K / 128;
+  const int nt = t.nt;
+
+  // Per-thread chunk c = tid + i * 512 sits in tile row tid / 8 + 64 i with the
+  // same 16-byte column tid % 8, so its LDS offset is the i = 0 offset plus
+  // i * 64 rows (the XOR swizzle depends on the row only through row & 7), and
+  // its global address is the i = 0 address plus a workgroup-uniform step.
+  // Addresses are 32-bit offsets from workgroup-uniform bases (a tile's rows
+  // and an expert's matrix are each < 4 GiB).
+  const int r0 = tid / (kF8BK / 16);
+  const int kc0 = tid % (kF8BK / 16);
+  const int lds0 = lds8_off(r0, kc0);
+  constexpr int kLdsStep = (kF8Threads / (kF8BK / 16)) * kF8BK;   // 64 rows
+  const uint8_t* a_base = g.A + (t.row_begin + t.m_off) * static_cast<int64_t>(K);
+  uint32_t a_off[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    int r = r0 + i * (kF8Threads / (kF8BK / 16));
+    r = t.m_off + r < t.rows ? r : t.rows - 1 - t.m_off;
+    a_off[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) + kc0 * 16;
+  }
+  const uint8_t* be = g.B + static_cast<size_t>(t.e) * g.b_rows * K;
+  const uint32_t b_off0 = static_cast<uint32_t>(f8_b_row<MODE>(g, nt, r0)) * static_cast<uint32_t>(K) + kc0 * 16;
+  // weight row of chunk i minus that of chunk 0 (uniform)
+  auto b_step = [&](int i) -> uint32_t {
+    return static_cast<uint32_t>(f8_b_row<MODE>(g, nt, i * (kF8Threads / (kF8BK / 16))) - f8_b_row<MODE>(g, nt, 0)) *
+           static_cast<uint32_t>(K);
+  };
+  // E8M0 bytes of the activation rows this lane feeds to the MFMA (row l % 16
+  // of each 16-row subtile; rows past the expert's end read its last row).
+  const int frag_row = lane & 15;
+  const uint8_t* as_base = g.As + t.row_begin * static_cast<int64_t>(KB);
+  const int as_row0 = t.m_off + wm * WM + frag_row;
+  // Weight block scales: gate and up blocks (gate/up) or the wave's 128-row block (down).
+  const float* bs_e = g.Bs + static_cast<size_t>(t.e) * (g.b_rows / 128) * KB;
+  const float* ws0;
+  const float* ws1;
+  if constexpr (MODE == MODE_GATEUP) {
+    ws0 = bs_e + static_cast<size_t>(nt) * KB;
+    ws1 = bs_e + static_cast<size_t>(g.N / 128 + nt) * KB;
+  } else {
+    ws0 = bs_e + static_cast<size_t>((nt * kF8BN + wn * WN) / 128) * KB;
+    ws1 = ws0;
+  }
+
+  u32x4_t ra0[CA], rb0[CB], ra1[CA], rb1[CB];
+  uint32_t sa0[TM], sa1[TM];
+  float sw0[2], sw1[2];
+  auto load_data = [&](int kt, u32x4_t* ra, u32x4_t* rb) {
+    const uint32_t k0 = static_cast<uint32_t>(kt) * kF8BK;
+#pragma unroll
+    for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_base + (a_off[i] + k0));
+#pragma unroll
+    for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(be + (b_off0 + b_step(i) + k0));
+  };
+  auto load_scales = [&](int kt, uint32_t* sa, float* sw) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int mr = min(as_row0 + tm * 16, t.rows - 1);
+      sa[tm] = as_base[static_cast<uint32_t>(mr) * static_cast<uint32_t>(KB) + kt];
+    }
+    sw[0] = ws0[kt];
+    sw[1] = ws1[kt];
+  };
+  auto store_stage = [&](int buf, const u32x4_t* ra, const u32x4_t* rb) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<u32x4_t*>(&sA[buf][lds0 + i * kLdsStep]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) *reinterpret_cast<u32x4_t*>(&sB[buf][lds0 + i * kLdsStep]) = rb[i];
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int frag_q = lane >> 4;             // 32-byte K slice of the stage
+  const int tm_valid = __builtin_amdgcn_readfirstlane(
+      max(0, min(TM, (t.rows - t.m_off - wm * WM + 15) / 16)));
+  auto frag = [&](const uint8_t* base, int row) {
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(base + lds8_off(row, 2 * frag_q));
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(base + lds8_off(row, 2 * frag_q + 1));
+    return i32x8_t{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                   static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                   static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+  };
+  // One 16-row subtile at a time: its TN MFMAs, then their promotion into the
+  // accumulators, so at most TN products are live (the scheduling barrier
+  // keeps the compiler from hoisting the next subtile's MFMAs above them).
+  auto compute_stage = [&](int buf, const uint32_t* sa, const float* sw) {
+    i32x8_t bfv[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) bfv[tn] = frag(sB[buf], f8_b_lds_row<MODE, WN, TN>(wn, tn) + frag_row);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      if (tm < tm_valid) {
+        const i32x8_t af = frag(sA[buf], wm * WM + tm * 16 + frag_row);
+        f32x4_t pr[TN];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          pr[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af, bfv[tn], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, static_cast<int>(sa[tm]), 0, 127);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          acc[tm][tn] += pr[tn] * ((MODE == MODE_GATEUP && tn >= TN / 2) ? sw[1] : sw[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Two-deep register ring (see the bf16 kernel): stage s is loaded into slot
+  // s % 2 two stages before its MFMAs and stored to LDS buffer s % 2 one stage
+  // before them; steady-state loads are unconditional.  A slot's scales are
+  // reloaded right after the MFMAs that used them (one stage ahead).
+  load_data(0, ra0, rb0);
+  load_scales(0, sa0, sw0);
+  if (KT > 1) {
+    load_data(1, ra1, rb1);
+    load_scales(1, sa1, sw1);
+  }
+  store_stage(0, ra0, rb0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 3 < KT; kt += 2) {
+    load_data(kt + 2, ra0, rb0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage(0, sa0, sw0);
+    load_scales(kt + 2, sa0, sw0);
+    store_stage(1, ra1, rb1);
+    __syncthreads();
+    load_data(kt + 3, ra1, rb1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage(1, sa1, sw1);
+    load_scales(kt + 3, sa1, sw1);
+    store_stage(0, ra0, rb0);
+    __syncthreads();
+  }
+  const int left = KT - kt;                 // 1, 2 or 3 stages; stage kt is in LDS buffer 0
+  if (left == 3) {
+    load_data(kt + 2, ra0, rb0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage(0, sa0, sw0);
+    load_scales(kt + 2, sa0, sw0);
+    store_stage(1, ra1, rb1);
+    __syncthreads();
+    compute_stage(1, sa1, sw1);
+    store_stage(0, ra0, rb0);
+    __syncthreads();
+    compute_stage(0, sa0, sw0);
+  } else if (left == 2) {
+    compute_stage(0, sa0, sw0);
+    store_stage(1, ra1, rb1);
+    __syncthreads();
+    compute_stage(1, sa1, sw1);
+  } else {
+    compute_stage(0, sa0, sw0);
+  }
+
+  // Epilogue.  Accumulator element r of lane l in a 16x16 tile is
+  // (row 4*(l/16) + r, column l%16).
+  const int col_in = lane & 15;
+  const int row_q = (lane >> 4) * 4;
+  if constexpr (MODE == MODE_GATEUP) {
+    // h = silu(gate) * up, then per row: amax over the tile's 128 h columns
+    // (this wave's WN/2 columns in registers and lanes, the other waves'
+    // through LDS), E8M0 scale, E4M3 codes.
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN / 2; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[tm][tn][r] = silu_f32(acc[tm][tn][r]) * acc[tm][tn + TN / 2][r];
+    float* s_amax = reinterpret_cast<float*>(&sA[0][0]);   // [WAVES_N][BM]
+    __syncthreads();                                       // every wave is done with the LDS tiles
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float m = 0.f;
+#pragma unroll
+        for (int tn = 0; tn < TN / 2; ++tn) m = fmaxf(m, fabsf(acc[tm][tn][r]));
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+        if (col_in == 0) s_amax[wn * BM + wm * WM + tm * 16 + row_q + r] = m;
+      }
+    __syncthreads();
+    uint8_t* Cq = static_cast<uint8_t*>(g.C);
+    const int groups = g.N / kQGroup;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = wm * WM + tm * 16 + row_q + r;
+        const int mr = t.m_off + lr;
+        float m = 0.f;
+#pragma unroll
+        for (int w = 0; w < S::WAVES_N; ++w) m = fmaxf(m, s_amax[w * BM + lr]);
+        const uint32_t b = e8m0_for_amax(m);
+        const float inv = e8m0_inv_scale(b);
+        if (mr < t.rows) {
+          const int64_t row = t.row_begin + mr;
+#pragma unroll
+          for (int tn = 0; tn < TN / 2; ++tn) {
+            const int col = nt * (kF8BN / 2) + wn * (WN / 2) + tn * 16 + col_in;
+            Cq[row * g.N + col] = fp8_rne1(acc[tm][tn][r] * inv);
+          }
+          if (wn == 0 && col_in == 0) g.Cs[row * groups + nt] = static_cast<uint8_t>(b);
+        }
+      }
+  } else {
+    bf16_t* C = static_cast<bf16_t*>(g.C);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int col = nt * kF8BN + wn * WN + tn * 16 + col_in;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
+          if (mr < t.rows) C[(t.row_begin + mr) * g.N + col] = f32_to_bf16(acc[tm][tn][r]);
+        }
+      }
+  }
+}
+
+template <int BM, int MODE>
+__global__ __launch_bounds__(kF8Threads, 2) void k_gemm_f8(F8Params p) {
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * kF8BK];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][kF8BN * kF8BK];
+  int* s_loc = reinterpret_cast<int*>(&sA[0][0]);   // tile location, before sA holds A tiles
+  TileLoc t;
+  if (!locate_tile<BM>(p.loc, s_loc, t)) return;
+  __syncthreads();                                  // s_loc read by all before sA is filled
+  gemm_tile_f8<BM, MODE>(p.g, t, sA, sB);
+}
+
+}  // namespace dbomoe

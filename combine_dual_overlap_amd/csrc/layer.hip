@@ -37,7 +37,7 @@ namespace dbomoe {
 namespace {
 
 enum Buf { B_LOGITS, B_IDS, B_W, B_COUNTS, B_OFFSETS, B_TILE_OFF, B_PERM, B_INV, B_XPERM, B_YPERM,
-           B_SHOUT, B_DISPWS, B_ROUTEWS, B_H, B_SHH, B_COUNT };
+           B_SHOUT, B_DISPWS, B_ROUTEWS, B_H, B_SHH, B_XSCALE, B_COUNT };
 
 struct HalfLayout {
   size_t off[B_COUNT];
@@ -64,14 +64,16 @@ HalfLayout half_layout(const moe_layer_desc* d, int64_t T) {
   sz[B_TILE_OFF] = static_cast<size_t>(E_loc + 1) * 4;
   sz[B_PERM] = static_cast<size_t>(cap) * 4;
   sz[B_INV] = static_cast<size_t>(cap) * 4;
-  sz[B_XPERM] = static_cast<size_t>(cap) * d->H * as;
+  const bool f8 = d->fp8_act != 0;
+  sz[B_XPERM] = static_cast<size_t>(cap) * d->H * (f8 ? 1 : as);
+  sz[B_XSCALE] = f8 ? static_cast<size_t>(cap) * (d->H / 128) : 0;
   sz[B_YPERM] = static_cast<size_t>(cap) * d->H * as;
   sz[B_SHOUT] = d->shared_I > 0
                     ? static_cast<size_t>(dense_down_chunks(d->act, d->shared_I, d->I)) * T * d->H * as
                     : 0;
   sz[B_DISPWS] = dispatch_ws_bytes(T, k, E_loc);
   sz[B_ROUTEWS] = route_ws_bound(T, E);
-  sz[B_H] = ffn_ws_bytes(cap, d->I, d->act);
+  sz[B_H] = f8 ? ffn_fp8_ws_bytes(cap, d->I) : ffn_ws_bytes(cap, d->I, d->act);
   sz[B_SHH] = d->shared_I > 0 ? ffn_ws_bytes(T, d->shared_I, d->act) : 0;
   HalfLayout L;
   size_t o = 0;
@@ -92,6 +94,12 @@ moe_status check_desc(const moe_layer_desc* d) {
   const int E_loc = d->expert_end - d->expert_begin;
   st = check_ffn_shapes(d->act, d->wdt, d->H, d->I, E_loc, d->w13_scale, d->w2_scale);
   if (st != MOE_OK) return st;
+  if (d->fp8_act != 0 && d->fp8_act != 1) return MOE_ERR_INVALID_ARG;
+  if (d->fp8_act) {
+    if (d->act != MOE_BF16 || d->wdt != MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
+    st = check_ffn_fp8_shapes(d->H, d->I, E_loc, d->w13_scale, d->w2_scale);
+    if (st != MOE_OK) return st;
+  }
   if (!d->w_router || !d->w13 || !d->w2) return MOE_ERR_INVALID_ARG;
   if (!aligned16(d->w_router) || !aligned16(d->w13) || !aligned16(d->w2) ||
       (d->w13_scale && !aligned16(d->w13_scale)) || (d->w2_scale && !aligned16(d->w2_scale)))
@@ -149,7 +157,8 @@ struct HipBackend {
         DispatchArgs a{xm, d->act, T, d->H, buf<int32_t>(mb, B_IDS), k, d->route.E, d->expert_begin,
                        d->expert_end, 0, buf<int32_t>(mb, B_COUNTS), buf<int32_t>(mb, B_OFFSETS),
                        nullptr, buf<int32_t>(mb, B_PERM), buf<int32_t>(mb, B_INV),
-                       buf<void>(mb, B_XPERM), buf<void>(mb, B_DISPWS), o->comm_cu_budget};
+                       buf<void>(mb, B_XPERM), buf<void>(mb, B_DISPWS), o->comm_cu_budget,
+                       d->fp8_act ? buf<uint8_t>(mb, B_XSCALE) : nullptr};
         if (ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][3], s) != hipSuccess) return MOE_ERR_HIP;
         st = launch_dispatch(a, s);
         if (st == MOE_OK && ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][4], s) != hipSuccess)
@@ -162,6 +171,7 @@ struct HipBackend {
         const int64_t hint = (T * k + d->route.E - 1) / d->route.E;
         FfnArgs a{};
         a.x = buf<void>(mb, B_XPERM);
+        a.xs = d->fp8_act ? buf<uint8_t>(mb, B_XSCALE) : nullptr;
         a.act = d->act;
         a.H = d->H;
         a.I = d->I;
@@ -350,6 +360,7 @@ extern "C" moe_status dbo_moe_layer(dbo_ctx* ctx, const moe_layer_desc* d, const
     return MOE_ERR_INVALID_ARG;
   if (o->ffn_tile_m == 16 && !ffn_ws_fits(d->act, d->H, d->I, d->shared_I > 0 ? 1 : 0, d->shared_I))
     return MOE_ERR_UNSUPPORTED;
+  if (d->fp8_act && o->ffn_tile_m != 0 && o->ffn_tile_m != 64 && o->ffn_tile_m != 128) return MOE_ERR_UNSUPPORTED;
   if (o->split_at != -1 && (o->split_at < 1 || o->split_at >= T)) return MOE_ERR_INVALID_ARG;
   for (auto& v : ctx->stats) v = 0;
   if (T == 0) return MOE_OK;

@@ -38,9 +38,10 @@ class DeviceLayer:
     w2, w13_scale, w2_scale, shared_w13, shared_w2 (CPU or device tensors) and
     `cfg` with the routing fields (E, k, score, renormalize, n_groups,
     topk_groups, group_topn, routed_scale, expert_begin, expert_end, H, I).
+    fp8_act: run the routed experts with fp8 activations (fp8 weights only).
     """
 
-    def __init__(self, inp: dict, device: str = "cuda", T_max: int = None):
+    def __init__(self, inp: dict, device: str = "cuda", T_max: int = None, fp8_act: bool = False):
         cfg = inp["cfg"]
         self.cfg = cfg
         d = torch.device(device)
@@ -60,7 +61,8 @@ class DeviceLayer:
         self.desc = B.moe_layer_desc(
             cfg.H, cfg.I, B.dtype_code(self.x), B.dtype_code(self.w13), self.route,
             cfg.expert_begin, cfg.expert_end, B.ptr(self.w_router), B.ptr(self.w13), B.ptr(self.w2),
-            B.ptr(self.w13_scale), B.ptr(self.w2_scale), shI, B.ptr(self.shared_w13), B.ptr(self.shared_w2))
+            B.ptr(self.w13_scale), B.ptr(self.w2_scale), shI, B.ptr(self.shared_w13), B.ptr(self.shared_w2),
+            int(bool(fp8_act)))
         self.T = self.x.shape[0]
         self.T_max = T_max or self.T
         nbytes = B.moe_layer_workspace_size(self.desc, self.T_max)

@@ -121,6 +121,31 @@ moe_status moe_dispatch(const void* x, moe_dtype act, int64_t T, int32_t H,
                         int32_t* perm, int32_t* inv, void* x_perm,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * fp8 activations: per-row quantisation in groups of 128 columns.
+ * The pages name a fused SiLU-mul + fp8 quantisation op that feeds an fp8
+ * GEMM ("[Core/DBO][1/N] Add Dual-Batch Overlap mechanism to VLLM", CI
+ * discussion) and give no rule.  Reading: a group of 128 consecutive columns
+ * of a row is stored as E4M3 (fn) codes plus one E8M0 byte b (scale 2^(b-127));
+ * b - 127 is the smallest e >= -127 with max|group| <= 448 * 2^e, and each
+ * code is the round-to-nearest-even E4M3 value of x * 2^-e (exact scaling, so
+ * the codes depend only on the values).  Real value = code value * 2^(b-127).
+ * Inputs must be finite.
+ *
+ * moe_quant_fp8_rows - quantise x [n, K] bf16 (K % 128 == 0, else
+ *   MOE_ERR_UNSUPPORTED) into q [n, K] codes and scale [n, K/128] bytes.
+ *
+ * moe_dispatch_fp8 - moe_dispatch (same arguments and outputs, act = bf16)
+ *   whose row gather quantises each token row once and writes its codes to
+ *   xq_perm [T*k, H] and its bytes to xq_scale [T*k, H/128].  H % 128 == 0.
+ * ------------------------------------------------------------------------- */
+moe_status moe_quant_fp8_rows(const void* x, int64_t n, int32_t K, uint8_t* q, uint8_t* scale, void* stream);
+moe_status moe_dispatch_fp8(const void* x, int64_t T, int32_t H, const int32_t* topk_ids, int32_t k,
+                            int32_t E_total, int32_t expert_begin, int32_t expert_end, int32_t tile_m,
+                            int32_t* counts, int32_t* offsets, int32_t* tile_offsets, int32_t* perm,
+                            int32_t* inv, uint8_t* xq_perm, uint8_t* xq_scale, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* Device error word of a dispatch workspace (0 = none, 1 = an expert id was
  * out of range).  Synchronises `stream` and copies 4 bytes: debug use only. */
 moe_status moe_get_device_error(const void* dispatch_ws, int32_t* code, void* stream);
@@ -166,6 +191,31 @@ moe_status moe_grouped_ffn(const void* x_perm, moe_dtype act, int32_t H, int32_t
                            void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_grouped_ffn_fp8 - moe_grouped_ffn with fp8 activations and fp8 weights:
+ * the fp8 expert path fed by the fused SiLU-mul + fp8 quantisation op
+ * ("[Core/DBO][1/N]", CI discussion).
+ *   xq_perm [cap_rows, H] E4M3 codes, xq_scale [cap_rows, H/128] E8M0 bytes
+ *            (moe_dispatch_fp8 / moe_quant_fp8_rows)
+ *   w13 [E_loc, 2I, H], w2 [E_loc, H, I] E4M3 codes with the fp32 128x128
+ *            block scales w13_scale / w2_scale (both required, positive)
+ *   y_perm   [cap_rows, H] bf16 out
+ *   tile_m   0 (automatic), 64 or 128 rows per tile; else MOE_ERR_UNSUPPORTED
+ *   ws       moe_ffn_fp8_workspace_size(cap_rows, I) bytes: h codes
+ *            [cap_rows, I] then (256-byte aligned) h bytes [cap_rows, I/128]
+ * h = silu(gate) * up is computed in fp32 and quantised as above (groups of
+ * 128 of its I columns) before the down projection.  fp8 x fp8 MFMAs with
+ * fp32 accumulation; each 128-wide K block's product is scaled by its weight
+ * block scale as it is accumulated.  H % 256 == 0 and I % 128 == 0, else
+ * MOE_ERR_UNSUPPORTED.  Same offsets / E_loc / dense rules as moe_grouped_ffn.
+ * ------------------------------------------------------------------------- */
+size_t moe_ffn_fp8_workspace_size(int64_t cap_rows, int32_t I);
+moe_status moe_grouped_ffn_fp8(const uint8_t* xq_perm, const uint8_t* xq_scale, int32_t H, int32_t I,
+                               const int32_t* offsets, int32_t E_loc, int64_t cap_rows,
+                               const uint8_t* w13, const uint8_t* w2, const float* w13_scale,
+                               const float* w2_scale, void* y_perm, int32_t tile_m, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * moe_combine - weighted gather-reduce, the single-GPU stand-in for the
  * all-to-all combine ("[Core/DBO][1/N]", Purpose).
  *   out[t] = sum_{j: inv[t*k+j] >= 0} topk_w[t, j] * y_perm[inv[t*k+j]]
@@ -200,6 +250,13 @@ typedef struct {
                                    intermediate dims stacked) */
   const void* shared_w13;       /* [2*shared_I, H] act */
   const void* shared_w2;        /* [H, shared_I] act */
+  int32_t fp8_act;              /* 0, or 1: the routed experts run with fp8 activations
+                                   (needs act MOE_BF16, wdt MOE_FP8_E4M3FN, H % 256 == 0,
+                                   I % 128 == 0): the dispatch writes rows as
+                                   moe_dispatch_fp8 does and the FFN is
+                                   moe_grouped_ffn_fp8 (row tiles 64 or 128: ffn_tile_m
+                                   0, 64 or 128, else MOE_ERR_UNSUPPORTED).  The shared
+                                   experts keep act. */
 } moe_layer_desc;
 
 typedef enum {
