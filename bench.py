@@ -292,7 +292,9 @@ def main():
     tile = args.ffn_tile_m or B.moe_ffn_auto_tile(B.dtype_code(L.x), B.dtype_code(L.w13), cfg.H, cfg.I,
                                                   -(-T_mb0 * cfg.k // cfg.E), T_mb0 if I_sh else 0, I_sh)
     if args.fp8_act:
-        tile = 128 if tile >= 128 else 64
+        m = -(-T_mb0 * cfg.k // cfg.E)
+        tile = (128 if args.ffn_tile_m >= 128 else 64) if args.ffn_tile_m else \
+            (64 if m + 3 * m ** 0.5 + 1 <= 64 else 128)
     kname = ("k_gemm_nt_f32 (fp32 SIMT)" if cfg.act == "f32" else
              f"k_gemm_f8 ({tile}-row LDS tiles, fp8 x fp8)" if args.fp8_act else
              "k_gemm_ws (weight-streaming, 16-row tiles)" if tile == 16 else f"k_gemm_nt ({tile}-row LDS tiles)")

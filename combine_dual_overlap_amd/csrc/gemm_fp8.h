@@ -35,6 +35,7 @@ namespace dbomoe {
 constexpr int kF8BK = 128;          // K per stage (= bytes per row per stage)
 constexpr int kF8BN = 256;          // weight rows per column tile
 constexpr int kF8Threads = 512;     // 8 waves
+constexpr int kF8MaxK = 128 * 128;  // K blocks of a weight scale row held in two registers per lane
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -148,9 +149,24 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
     ws1 = ws0;
   }
 
+  // The two weight scale rows, one K block per lane (lane l holds blocks l
+  // and l + 64), picked per stage with v_readlane: the K loop issues no
+  // scalar memory loads, whose completion counter the LDS reads share (a wait
+  // for an LDS read would otherwise also wait for a scale load in flight).
+  float wsv[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float* row = j == 0 ? ws0 : ws1;
+    wsv[j][0] = row[min(lane, KB - 1)];
+    wsv[j][1] = row[min(lane + 64, KB - 1)];
+  }
+  auto wscale = [&](int j, int kt) {
+    const float v = kt < 64 ? wsv[j][0] : wsv[j][1];
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kt & 63));
+  };
+
   u32x4_t ra0[CA], rb0[CB], ra1[CA], rb1[CB];
   uint32_t sa0[TM], sa1[TM];
-  float sw0[2], sw1[2];
   auto load_data = [&](int kt, u32x4_t* ra, u32x4_t* rb) {
     const uint32_t k0 = static_cast<uint32_t>(kt) * kF8BK;
 #pragma unroll
@@ -158,14 +174,12 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
 #pragma unroll
     for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(be + (b_off0 + b_step(i) + k0));
   };
-  auto load_scales = [&](int kt, uint32_t* sa, float* sw) {
+  auto load_scales = [&](int kt, uint32_t* sa) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       const int mr = min(as_row0 + tm * 16, t.rows - 1);
       sa[tm] = as_base[static_cast<uint32_t>(mr) * static_cast<uint32_t>(KB) + kt];
     }
-    sw[0] = ws0[kt];
-    sw[1] = ws1[kt];
   };
   auto store_stage = [&](int buf, const u32x4_t* ra, const u32x4_t* rb) {
 #pragma unroll
@@ -193,7 +207,8 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
   // One 16-row subtile at a time: its TN MFMAs, then their promotion into the
   // accumulators, so at most TN products are live (the scheduling barrier
   // keeps the compiler from hoisting the next subtile's MFMAs above them).
-  auto compute_stage = [&](int buf, const uint32_t* sa, const float* sw) {
+  auto compute_stage = [&](int buf, const uint32_t* sa, int kt_c) {
+    const float sw[2] = {wscale(0, kt_c), wscale(1, kt_c)};
     i32x8_t bfv[TN];
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) bfv[tn] = frag(sB[buf], f8_b_lds_row<MODE, WN, TN>(wn, tn) + frag_row);
@@ -219,10 +234,10 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
   // before them; steady-state loads are unconditional.  A slot's scales are
   // reloaded right after the MFMAs that used them (one stage ahead).
   load_data(0, ra0, rb0);
-  load_scales(0, sa0, sw0);
+  load_scales(0, sa0);
   if (KT > 1) {
     load_data(1, ra1, rb1);
-    load_scales(1, sa1, sw1);
+    load_scales(1, sa1);
   }
   store_stage(0, ra0, rb0);
   __syncthreads();
@@ -230,14 +245,14 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
   for (; kt + 3 < KT; kt += 2) {
     load_data(kt + 2, ra0, rb0);
     __builtin_amdgcn_sched_barrier(0);
-    compute_stage(0, sa0, sw0);
-    load_scales(kt + 2, sa0, sw0);
+    compute_stage(0, sa0, kt);
+    load_scales(kt + 2, sa0);
     store_stage(1, ra1, rb1);
     __syncthreads();
     load_data(kt + 3, ra1, rb1);
     __builtin_amdgcn_sched_barrier(0);
-    compute_stage(1, sa1, sw1);
-    load_scales(kt + 3, sa1, sw1);
+    compute_stage(1, sa1, kt + 1);
+    load_scales(kt + 3, sa1);
     store_stage(0, ra0, rb0);
     __syncthreads();
   }
@@ -245,21 +260,21 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
   if (left == 3) {
     load_data(kt + 2, ra0, rb0);
     __builtin_amdgcn_sched_barrier(0);
-    compute_stage(0, sa0, sw0);
-    load_scales(kt + 2, sa0, sw0);
+    compute_stage(0, sa0, kt);
+    load_scales(kt + 2, sa0);
     store_stage(1, ra1, rb1);
     __syncthreads();
-    compute_stage(1, sa1, sw1);
+    compute_stage(1, sa1, kt + 1);
     store_stage(0, ra0, rb0);
     __syncthreads();
-    compute_stage(0, sa0, sw0);
+    compute_stage(0, sa0, kt + 2);
   } else if (left == 2) {
-    compute_stage(0, sa0, sw0);
+    compute_stage(0, sa0, kt);
     store_stage(1, ra1, rb1);
     __syncthreads();
-    compute_stage(1, sa1, sw1);
+    compute_stage(1, sa1, kt + 1);
   } else {
-    compute_stage(0, sa0, sw0);
+    compute_stage(0, sa0, kt);
   }
 
   // Epilogue.  Accumulator element r of lane l in a 16x16 tile is

@@ -289,6 +289,21 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
     }
   }
 
+  // fp8: the two scale rows, one K block per lane (lane l holds blocks l and
+  // l + 64), picked per stage with v_readlane.  A scalar memory load inside the
+  // K loop would share its completion counter with the LDS reads, so every
+  // wait for an LDS read would also wait for the scale load in flight.
+  float scv[2][2] = {{1.f, 1.f}, {1.f, 1.f}};
+  if constexpr (FP8) {
+    const int kblocks = K / 128;
+    const int lane_l = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float* row = j == 0 ? srow0 : srow1;
+      scv[j][0] = row[min(lane_l, kblocks - 1)];
+      scv[j][1] = row[min(lane_l + 64, kblocks - 1)];
+    }
+  }
   u32x4_t ra0[CA], rb0[CB], ra1[CA], rb1[CB];
   float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};
   auto load_stage = [&](int kt, u32x4_t* ra, u32x4_t* rb, float* sc) {
@@ -301,8 +316,12 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
       rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + kb);
     }
     if constexpr (FP8) {
-      sc[0] = srow0[k0 / 128];
-      sc[1] = srow1[k0 / 128];
+      const int blk = k0 / 128;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float v = blk < 64 ? scv[j][0] : scv[j][1];
+        sc[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), blk & 63));
+      }
     }
   };
   auto store_stage = [&](int buf, const u32x4_t* ra, const u32x4_t* rb, const float* sc) {
