@@ -159,7 +159,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="layer configuration 1..5 (default 2)")
-    ap.add_argument("--schedule", default="dbo", choices=["dbo", "serial", "unsplit", "dbo_late_event"])
+    ap.add_argument("--schedule", default="dbo", choices=["dbo", "serial", "unsplit", "dbo_late_event", "dbo_recv_hook"])
     ap.add_argument("--comm-cu-budget", type=int, default=0)
     ap.add_argument("--ffn-tile-m", type=int, default=0,
                     help="expert FFN row tile: 0 automatic, 16 weight-streaming kernel, 32/64/128 LDS-tiled kernel")

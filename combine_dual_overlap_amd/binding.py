@@ -19,8 +19,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_MISALIGNED, MOE_ERR_WO
     0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16, MOE_FP8_E4M3FN = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-DBO_SCHED_UNSPLIT, DBO_SCHED_SERIAL, DBO_SCHED_DBO, DBO_SCHED_DBO_LATE_EVENT = 0, 1, 2, 3
-SCHEDULES = {"unsplit": 0, "serial": 1, "dbo": 2, "dbo_late_event": 3}
+DBO_SCHED_UNSPLIT, DBO_SCHED_SERIAL, DBO_SCHED_DBO, DBO_SCHED_DBO_LATE_EVENT, DBO_SCHED_DBO_RECV_HOOK = 0, 1, 2, 3, 4
+SCHEDULES = {"unsplit": 0, "serial": 1, "dbo": 2, "dbo_late_event": 3, "dbo_recv_hook": 4}
 
 EXPORTED = [
     "moe_route_workspace_size", "moe_route_topk", "moe_dispatch_workspace_size", "moe_dispatch",
@@ -29,6 +29,7 @@ EXPORTED = [
     "dbo_ctx_last_stats",
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "dbo_moe_layer", "moe_status_string",
     "moe_quant_fp8_rows", "moe_dispatch_fp8", "moe_ffn_fp8_workspace_size", "moe_grouped_ffn_fp8",
+    "moe_dispatch_send", "moe_dispatch_recv",
 ]
 
 
@@ -102,6 +103,9 @@ def lib():
             "moe_dispatch_fp8": (_i32, [_vp, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
             "moe_ffn_fp8_workspace_size": (_sz, [_i64, _i32]),
+            "moe_dispatch_send": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                         _vp, _sz, _vp]),
+            "moe_dispatch_recv": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
             "moe_grouped_ffn_fp8": (_i32, [_vp, _vp, _i32, _i32, _vp, _i32, _i64, _vp, _vp, _vp, _vp,
                                            _vp, _i32, _vp, _sz, _vp]),
         }
@@ -181,6 +185,21 @@ def moe_dispatch(x, topk_ids, E_total, expert_begin, expert_end, counts, offsets
                               tile_m, ptr(counts), ptr(offsets), ptr(tile_offsets), ptr(perm), ptr(inv),
                               ptr(x_perm), ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)),
            "moe_dispatch")
+
+
+def moe_dispatch_send(topk_ids, E_total, expert_begin, expert_end, counts, offsets, perm, inv, ws, tile_m=0,
+                      tile_offsets=None, stream=None):
+    T = topk_ids.shape[0]
+    k = topk_ids.shape[1] if topk_ids.dim() == 2 else 1
+    _check(lib().moe_dispatch_send(ptr(topk_ids), T, k, E_total, expert_begin, expert_end, tile_m, ptr(counts),
+                                   ptr(offsets), ptr(tile_offsets), ptr(perm), ptr(inv), ptr(ws),
+                                   ws.numel() * ws.element_size(), stream_handle(stream)), "moe_dispatch_send")
+
+
+def moe_dispatch_recv(x, k, inv, x_perm, xq_scale=None, stream=None):
+    T, H = x.shape
+    _check(lib().moe_dispatch_recv(ptr(x), dtype_code(x), T, H, k, ptr(inv), ptr(x_perm), ptr(xq_scale),
+                                   stream_handle(stream)), "moe_dispatch_recv")
 
 
 def moe_get_device_error(dispatch_ws, stream=None) -> int:

@@ -113,6 +113,10 @@ struct DispatchArgs {
 };
 size_t dispatch_ws_bytes(int64_t T, int32_t k, int32_t E_loc);
 moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s);
+// The two phases of launch_dispatch: send = count, scan and rank (counts,
+// offsets, perm, inv); recv = the row gather (x_perm, or fp8 rows + scales).
+moe_status launch_dispatch_send(const DispatchArgs& a, hipStream_t s);
+moe_status launch_dispatch_recv(const DispatchArgs& a, hipStream_t s);
 
 struct FfnArgs {
   const void* x; moe_dtype act; int32_t H; int32_t I;

@@ -21,6 +21,16 @@
 //   p3 comm:    wait ffn-event, combine, record combine-event
 // and finally the compute stream waits both combine events (comm work joined
 // back before anything that follows the layer on the compute stream).
+//
+// Receive-hook variant (the low-latency dispatch structure of "[Core/DBO][2/N]
+// Dual-Batch Overlap add DeepEP High Throughput support and Prefill support",
+// review of modular_kernel.py: the dispatch returns a receive hook, which
+// under DBO is registered with the microbatch and run after one more yield):
+// p1 becomes two phases on the comm stream,
+//   p1  comm: wait route-event, dispatch send (count, scan, rank), register hook   yield
+//   p1r comm: run the hook: dispatch receive (row gather), record recv-event       yield
+// and p2 waits for the recv-event.  Each microbatch yields four times, and the
+// comm stream carries A.send, B.send, A.recv, B.recv.
 #pragma once
 
 #include <cstdint>
@@ -30,8 +40,11 @@ namespace dbomoe {
 namespace sched {
 
 enum StreamId { kCompute = 0, kComm = 1 };
-enum Stage { kRoute = 0, kDispatch = 1, kFfn = 2, kCombine = 3, kNumStages = 4 };
-enum Schedule { kUnsplit = 0, kSerial = 1, kDbo = 2, kDboLate = 3 };
+// kDispatch is the whole dispatch; kDispatchSend + kDispatchRecv are its two
+// phases in the receive-hook schedule.
+enum Stage { kRoute = 0, kDispatch = 1, kFfn = 2, kCombine = 3, kDispatchSend = 4, kDispatchRecv = 5,
+             kNumStages = 6 };
+enum Schedule { kUnsplit = 0, kSerial = 1, kDbo = 2, kDboLate = 3, kDboRecvHook = 4 };
 
 struct Op {
   enum Kind { LAUNCH = 0, RECORD = 1, WAIT = 2, YIELD = 3 } kind;
@@ -64,8 +77,10 @@ inline void append_sequential(Plan& p, int mb) {
 
 // Phase `ph` of microbatch `mb` of the two-stream schedule.  `late`: the
 // compute-stream events that the comm stream waits on are recorded when the
-// microbatch resumes after its yield instead of before it.
-inline void append_phase(Plan& p, int mb, int ph, bool late) {
+// microbatch resumes after its yield instead of before it.  `hook`: the
+// receive-hook variant, whose phases are 0, 1, 4 (the hook), 2, 3.
+inline void append_phase(Plan& p, int mb, int ph, bool late, bool hook) {
+  const int ready = hook ? kDispatchRecv : kDispatch;   // the event the FFN waits for
   switch (ph) {
     case 0:
       p.ops.push_back(launch(kCompute, mb, kRoute));
@@ -74,11 +89,19 @@ inline void append_phase(Plan& p, int mb, int ph, bool late) {
     case 1:
       if (late) p.ops.push_back(record(kCompute, mb, kRoute));
       p.ops.push_back(wait(kComm, mb, kRoute));
-      p.ops.push_back(launch(kComm, mb, kDispatch));
-      p.ops.push_back(record(kComm, mb, kDispatch));
+      if (hook) {
+        p.ops.push_back(launch(kComm, mb, kDispatchSend));   // the receive hook is registered here
+      } else {
+        p.ops.push_back(launch(kComm, mb, kDispatch));
+        p.ops.push_back(record(kComm, mb, kDispatch));
+      }
+      break;
+    case 4:   // the microbatch resumes and runs its receive hook
+      p.ops.push_back(launch(kComm, mb, kDispatchRecv));
+      p.ops.push_back(record(kComm, mb, kDispatchRecv));
       break;
     case 2:
-      p.ops.push_back(wait(kCompute, mb, kDispatch));
+      p.ops.push_back(wait(kCompute, mb, ready));
       p.ops.push_back(launch(kCompute, mb, kFfn));
       if (!late) p.ops.push_back(record(kCompute, mb, kFfn));
       break;
@@ -89,7 +112,7 @@ inline void append_phase(Plan& p, int mb, int ph, bool late) {
       p.ops.push_back(record(kComm, mb, kCombine));
       break;
   }
-  if (ph < 3) {
+  if (ph != 3) {
     p.ops.push_back(yield(mb));
     p.yields[mb]++;
   }
@@ -109,8 +132,13 @@ inline Plan build_plan(int schedule) {
     return p;
   }
   const bool late = schedule == kDboLate;
-  for (int ph = 0; ph < 4; ++ph)
-    for (int mb = 0; mb < 2; ++mb) append_phase(p, mb, ph, late);
+  const bool hook = schedule == kDboRecvHook;
+  const int order_plain[4] = {0, 1, 2, 3};
+  const int order_hook[5] = {0, 1, 4, 2, 3};
+  const int* order = hook ? order_hook : order_plain;
+  const int n_ph = hook ? 5 : 4;
+  for (int i = 0; i < n_ph; ++i)
+    for (int mb = 0; mb < 2; ++mb) append_phase(p, mb, order[i], late, hook);
   p.ops.push_back(wait(kCompute, 0, kCombine));
   p.ops.push_back(wait(kCompute, 1, kCombine));
   return p;

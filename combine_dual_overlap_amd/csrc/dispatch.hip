@@ -397,7 +397,7 @@ static moe_status launch_gather(const DispatchArgs& a, hipStream_t s) {
   return MOE_OK;
 }
 
-moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+moe_status launch_dispatch_send(const DispatchArgs& a, hipStream_t s) {
   const int E_loc = a.e_end - a.e_begin;
   const int64_t n_pairs = a.T * a.k;
   const int64_t nb = n_pair_blocks(a.T, a.k);
@@ -407,8 +407,7 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
                        a.tile_m > 0 ? a.tile_m : 1, a.counts, a.offsets, a.tile_m > 0 ? a.tile_offsets : nullptr,
                        a.perm, a.inv, w.err);
     DBOMOE_CHECK_LAUNCH();
-    if (nb == 0) return MOE_OK;
-    return launch_gather(a, s);
+    return MOE_OK;
   }
   if (nb > 0) {
     hipLaunchKernelGGL(k_disp_count, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a.ids, n_pairs,
@@ -425,7 +424,18 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_disp_rank, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a.ids, n_pairs, a.e_begin,
                      E_loc, w.block_hist, a.offsets, a.perm, a.inv);
   DBOMOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+moe_status launch_dispatch_recv(const DispatchArgs& a, hipStream_t s) {
+  if (a.T == 0) return MOE_OK;
   return launch_gather(a, s);
+}
+
+moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  const moe_status st = launch_dispatch_send(a, s);
+  if (st != MOE_OK) return st;
+  return launch_dispatch_recv(a, s);
 }
 
 }  // namespace dbomoe
@@ -461,6 +471,50 @@ extern "C" moe_status moe_dispatch(const void* x, moe_dtype act, int64_t T, int3
   DispatchArgs a{x, act, T, H, topk_ids, k, E_total, expert_begin, expert_end, tile_m,
                  counts, offsets, tile_offsets, perm, inv, x_perm, ws, 0, nullptr};
   return launch_dispatch(a, as_stream(stream));
+}
+
+extern "C" moe_status moe_dispatch_send(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E_total,
+                                        int32_t expert_begin, int32_t expert_end, int32_t tile_m, int32_t* counts,
+                                        int32_t* offsets, int32_t* tile_offsets, int32_t* perm, int32_t* inv,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || k > 16 || E_total < 1) return MOE_ERR_INVALID_ARG;
+  if (expert_begin < 0 || expert_end <= expert_begin || expert_end > E_total) return MOE_ERR_INVALID_ARG;
+  const int E_loc = expert_end - expert_begin;
+  if (E_loc > kMaxELoc) return MOE_ERR_UNSUPPORTED;
+  if (tile_offsets && tile_m <= 0) return MOE_ERR_INVALID_ARG;
+  if (!counts || !offsets || !ws) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !perm || !inv)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(topk_ids) || !aligned16(counts) || !aligned16(offsets) ||
+      (tile_offsets && !aligned16(tile_offsets)) || !aligned16(perm) || !aligned16(inv) || !aligned256(ws))
+    return MOE_ERR_MISALIGNED;
+  if (T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < dispatch_ws_bytes(T, k, E_loc)) return MOE_ERR_WORKSPACE;
+  DispatchArgs a{nullptr, MOE_BF16, T, 0, topk_ids, k, E_total, expert_begin, expert_end, tile_m,
+                 counts, offsets, tile_offsets, perm, inv, nullptr, ws, 0, nullptr};
+  return launch_dispatch_send(a, as_stream(stream));
+}
+
+extern "C" moe_status moe_dispatch_recv(const void* x, moe_dtype act, int64_t T, int32_t H, int32_t k,
+                                        const int32_t* inv, void* x_perm, uint8_t* xq_scale, void* stream) {
+  if (T < 0 || H <= 0 || k < 1 || k > 16) return MOE_ERR_INVALID_ARG;
+  if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (xq_scale && (act != MOE_BF16 || H % kQGroup)) return MOE_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(H) * dtype_size(act)) % 16) return MOE_ERR_MISALIGNED;
+  if (T == 0) return MOE_OK;
+  if (!x || !inv || !x_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(inv) || !aligned16(x_perm) || (xq_scale && !aligned16(xq_scale)))
+    return MOE_ERR_MISALIGNED;
+  if (T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  DispatchArgs a{};
+  a.x = x;
+  a.act = act;
+  a.T = T;
+  a.H = H;
+  a.k = k;
+  a.inv = const_cast<int32_t*>(inv);
+  a.x_perm = x_perm;
+  a.x_scale = xq_scale;
+  return launch_dispatch_recv(a, as_stream(stream));
 }
 
 extern "C" moe_status moe_dispatch_fp8(const void* x, int64_t T, int32_t H, const int32_t* topk_ids, int32_t k,

@@ -153,15 +153,23 @@ struct HipBackend {
         st = launch_route(a, s);
         break;
       }
-      case sched::kDispatch: {
+      case sched::kDispatch:
+      case sched::kDispatchSend:
+      case sched::kDispatchRecv: {
         DispatchArgs a{xm, d->act, T, d->H, buf<int32_t>(mb, B_IDS), k, d->route.E, d->expert_begin,
                        d->expert_end, 0, buf<int32_t>(mb, B_COUNTS), buf<int32_t>(mb, B_OFFSETS),
                        nullptr, buf<int32_t>(mb, B_PERM), buf<int32_t>(mb, B_INV),
                        buf<void>(mb, B_XPERM), buf<void>(mb, B_DISPWS), o->comm_cu_budget,
                        d->fp8_act ? buf<uint8_t>(mb, B_XSCALE) : nullptr};
-        if (ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][3], s) != hipSuccess) return MOE_ERR_HIP;
-        st = launch_dispatch(a, s);
-        if (st == MOE_OK && ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][4], s) != hipSuccess)
+        // timing: from the first dispatch kernel to the last (send start .. recv end)
+        if (stage != sched::kDispatchRecv && ctx->timing &&
+            hipEventRecord(ctx->tev[ctx->slot][mb][3], s) != hipSuccess)
+          return MOE_ERR_HIP;
+        st = stage == sched::kDispatch       ? launch_dispatch(a, s)
+             : stage == sched::kDispatchSend ? launch_dispatch_send(a, s)
+                                             : launch_dispatch_recv(a, s);
+        if (st == MOE_OK && stage != sched::kDispatchSend && ctx->timing &&
+            hipEventRecord(ctx->tev[ctx->slot][mb][4], s) != hipSuccess)
           return MOE_ERR_HIP;
         break;
       }
@@ -353,7 +361,7 @@ extern "C" moe_status dbo_moe_layer(dbo_ctx* ctx, const moe_layer_desc* d, const
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
-  if (o->schedule < DBO_SCHED_UNSPLIT || o->schedule > DBO_SCHED_DBO_LATE_EVENT) return MOE_ERR_INVALID_ARG;
+  if (o->schedule < DBO_SCHED_UNSPLIT || o->schedule > DBO_SCHED_DBO_RECV_HOOK) return MOE_ERR_INVALID_ARG;
   if (o->min_tokens_to_split < 0 || o->comm_cu_budget < 0) return MOE_ERR_INVALID_ARG;
   if (o->ffn_tile_m != 0 && o->ffn_tile_m != 16 && o->ffn_tile_m != 32 && o->ffn_tile_m != 64 &&
       o->ffn_tile_m != 128)

@@ -146,6 +146,28 @@ moe_status moe_dispatch_fp8(const void* x, int64_t T, int32_t H, const int32_t* 
                             int32_t* inv, uint8_t* xq_perm, uint8_t* xq_scale, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* ---------------------------------------------------------------------------
+ * moe_dispatch_send / moe_dispatch_recv - moe_dispatch in two phases, the
+ * send / receive-hook split of a low-latency dispatch ("[Core/DBO][2/N]
+ * Dual-Batch Overlap add DeepEP High Throughput support and Prefill support",
+ * review of modular_kernel.py: the dispatch returns a hook that the receiver
+ * runs later; under DBO after a yield).
+ *   send: topk_ids -> counts, offsets, tile_offsets, perm, inv (as
+ *         moe_dispatch; same workspace and device error word); no row moves.
+ *   recv: x [T, H] act and the send's inv [T*k] -> x_perm rows
+ *         (x_perm[inv[t*k+j]] = x[t] for inv >= 0).  xq_scale NULL: x_perm is
+ *         in act; else (act bf16, H % 128 == 0) x_perm receives E4M3 codes and
+ *         xq_scale [T*k, H/128] the E8M0 bytes, as moe_dispatch_fp8.
+ * send then recv on one stream equals moe_dispatch (moe_dispatch_fp8) bit for
+ * bit.
+ * ------------------------------------------------------------------------- */
+moe_status moe_dispatch_send(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E_total,
+                             int32_t expert_begin, int32_t expert_end, int32_t tile_m, int32_t* counts,
+                             int32_t* offsets, int32_t* tile_offsets, int32_t* perm, int32_t* inv,
+                             void* ws, size_t ws_bytes, void* stream);
+moe_status moe_dispatch_recv(const void* x, moe_dtype act, int64_t T, int32_t H, int32_t k,
+                             const int32_t* inv, void* x_perm, uint8_t* xq_scale, void* stream);
+
 /* Device error word of a dispatch workspace (0 = none, 1 = an expert id was
  * out of range).  Synchronises `stream` and copies 4 bytes: debug use only. */
 moe_status moe_get_device_error(const void* dispatch_ws, int32_t* code, void* stream);
@@ -264,9 +286,15 @@ typedef enum {
   DBO_SCHED_SERIAL = 1,         /* microbatch A fully, then B, compute stream only */
   DBO_SCHED_DBO = 2,            /* interleaved on two streams, events recorded before
                                    each yield (the fixed behaviour) */
-  DBO_SCHED_DBO_LATE_EVENT = 3  /* diagnostic: events recorded after the yield, so a
+  DBO_SCHED_DBO_LATE_EVENT = 3, /* diagnostic: events recorded after the yield, so a
                                    microbatch's comm also waits for the other
                                    microbatch's compute (the behaviour the fix removed) */
+  DBO_SCHED_DBO_RECV_HOOK = 4   /* DBO with the dispatch in two phases: send (count,
+                                   scan, rank), then a receive hook (the row gather) run
+                                   after one more yield, the low-latency dispatch structure
+                                   ("[Core/DBO][2/N] Dual-Batch Overlap add DeepEP High
+                                   Throughput support and Prefill support", review of
+                                   modular_kernel.py).  Four yields per microbatch */
 } dbo_schedule;
 
 typedef struct {
@@ -299,7 +327,8 @@ moe_status dbo_ctx_ffn_times(dbo_ctx* ctx, int32_t back, float* ms4);
  * B combine} (each step's kernels from the first launch to the last). */
 moe_status dbo_ctx_comm_times(dbo_ctx* ctx, int32_t back, float* ms4);
 /* Schedule bookkeeping of the last call: stats[0..5] = {schedule run, T0,
- * yields A, yields B, stages launched, events recorded}. */
+ * yields A, yields B, stages launched, events recorded}.  DBO issues 3 yields
+ * per microbatch, the receive-hook schedule 4. */
 moe_status dbo_ctx_last_stats(dbo_ctx* ctx, int64_t* stats6);
 
 /* Workspace of one call with up to T_max tokens: two disjoint halves, one per

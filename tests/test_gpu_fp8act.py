@@ -120,6 +120,32 @@ def test_dispatch_fp8_matches_oracle(cid):
     assert np.array_equal(xs.cpu().numpy()[:M].astype(np.int64), e + 127)
 
 
+def test_dispatch_send_recv_fp8_equals_one_call():
+    B = _B()
+    inp, ov = inputs(3, True)
+    cfg = inp["cfg"]
+    ids = torch.from_numpy(O.moe_layer_expert(ov, tokens=np.arange(1))["ids"].astype(np.int32)).cuda()
+    T, k, E_loc = cfg.T, cfg.k, cfg.E_loc
+    x = inp["x"].cuda()
+    outs = []
+    for two_phase in (False, True):
+        i32 = lambda n: torch.full((n,), -7, dtype=torch.int32, device="cuda")
+        counts, offsets, perm, inv = i32(E_loc), i32(E_loc + 1), i32(T * k), i32(T * k)
+        xq = torch.zeros(T * k, cfg.H, dtype=torch.uint8, device="cuda")
+        xs = torch.zeros(T * k, cfg.H // 128, dtype=torch.uint8, device="cuda")
+        ws = torch.empty(B.moe_dispatch_workspace_size(T, k, E_loc), dtype=torch.uint8, device="cuda")
+        if two_phase:
+            B.moe_dispatch_send(ids, cfg.E, cfg.expert_begin, cfg.expert_end, counts, offsets, perm, inv, ws)
+            B.moe_dispatch_recv(x, k, inv, xq, xq_scale=xs)
+        else:
+            B.moe_dispatch_fp8(x, ids, cfg.E, cfg.expert_begin, cfg.expert_end, counts, offsets, perm, inv, xq,
+                               xs, ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (counts, offsets, perm, inv, xq, xs)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def _ffn_fp8(B, xq, xs, I, offsets, E_loc, w13, w2, s13, s2, tile_m=0):
     cap, H = xq.shape
     y = torch.full((cap, H), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -207,7 +233,7 @@ def _gpu_ids(L, cfg, T0):
 
 
 @pytest.mark.parametrize("cid", [3, 4])
-@pytest.mark.parametrize("schedule", ["serial", "dbo"])
+@pytest.mark.parametrize("schedule", ["serial", "dbo", "dbo_recv_hook"])
 def test_layer_fp8act_small(cid, schedule):
     inp, ov = inputs(cid, True)
     cfg = inp["cfg"]

@@ -65,7 +65,7 @@ def test_route_ties_pick_lower_index():
     assert torch.allclose(w.cpu(), w.cpu()[:, :1].expand(8, 4))
 
 
-def _dispatch(C, cfg, x, ids, tile_m=16):
+def _dispatch(C, cfg, x, ids, tile_m=16, two_phase=False):
     B = C.binding
     T = x.shape[0]
     E_loc = cfg.expert_end - cfg.expert_begin
@@ -77,8 +77,13 @@ def _dispatch(C, cfg, x, ids, tile_m=16):
     inv = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
     x_perm = torch.zeros(cap, cfg.H, dtype=x.dtype, device="cuda")
     ws = torch.empty(B.moe_dispatch_workspace_size(T, cfg.k, E_loc), dtype=torch.uint8, device="cuda")
-    B.moe_dispatch(x, ids, cfg.E, cfg.expert_begin, cfg.expert_end, counts, offsets, perm, inv, x_perm, ws,
-                   tile_m=tile_m, tile_offsets=toff)
+    if two_phase:       # send (count, scan, rank), then the receive hook (row gather)
+        B.moe_dispatch_send(ids, cfg.E, cfg.expert_begin, cfg.expert_end, counts, offsets, perm, inv, ws,
+                            tile_m=tile_m, tile_offsets=toff)
+        B.moe_dispatch_recv(x, cfg.k, inv, x_perm)
+    else:
+        B.moe_dispatch(x, ids, cfg.E, cfg.expert_begin, cfg.expert_end, counts, offsets, perm, inv, x_perm, ws,
+                       tile_m=tile_m, tile_offsets=toff)
     torch.cuda.synchronize()
     return dict(counts=counts, offsets=offsets, tile_offsets=toff, perm=perm, inv=inv, x_perm=x_perm, ws=ws)
 
@@ -123,13 +128,14 @@ def test_dispatch(cid, small):
                                          (257, 6, 64, 0, 64), (64, 16, 300, 100, 300),
                                          (1024, 8, 64, 0, 64), (1025, 8, 64, 0, 64),
                                          (2048, 4, 256, 0, 256), (1000, 3, 300, 0, 257)])
-def test_dispatch_shapes(T, k, E, lo, hi):
+@pytest.mark.parametrize("two_phase", [False, True])
+def test_dispatch_shapes(T, k, E, lo, hi, two_phase):
     C = _gpu()
     rng = np.random.default_rng(T * 31 + k)
     cfg = W.LayerConfig("d", T=T, H=128, E=E, k=k, I=64, act="bf16", wdt="bf16", expert_begin=lo, expert_end=hi)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     x = torch.randn(T, 128).to(torch.bfloat16)
-    g = _dispatch(C, cfg, x.cuda(), torch.from_numpy(ids).cuda())
+    g = _dispatch(C, cfg, x.cuda(), torch.from_numpy(ids).cuda(), two_phase=two_phase)
     _check_dispatch(cfg, x, ids, g)
 
 

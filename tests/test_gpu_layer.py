@@ -11,7 +11,7 @@ from helpers import assert_close, check_routing, inputs, to_f64, tol_for
 
 pytestmark = pytest.mark.gpu
 
-SCHEDULES = ["unsplit", "serial", "dbo", "dbo_late_event"]
+SCHEDULES = ["unsplit", "serial", "dbo", "dbo_late_event", "dbo_recv_hook"]
 
 
 def _layer(inp, **kw):
@@ -57,7 +57,7 @@ def test_layer_small(cid, schedule):
     T0 = None if schedule == "unsplit" else (cfg.T + 1) // 2
     assert st["T0"] == (cfg.T if T0 is None else T0)
     if schedule.startswith("dbo"):
-        assert st["yields_a"] == st["yields_b"] == 3
+        assert st["yields_a"] == st["yields_b"] == (4 if schedule == "dbo_recv_hook" else 3)
     ids = _gpu_routing(L, cfg, ov, T0)
     ref = _reference(ov, ids)
     assert_close(to_f64(out), ref["out"], tol_for(cfg), f"out {cfg.name} {schedule}", ref["scale"])
@@ -68,7 +68,7 @@ def test_dbo_equals_serial_bitwise_and_repeatable(cid):
     inp, _ = inputs(cid, True)
     L = _layer(inp)
     base = L.run("serial").clone()
-    for sched in ["dbo", "dbo_late_event"] + ["dbo"] * 18:
+    for sched in ["dbo", "dbo_late_event", "dbo_recv_hook"] + ["dbo"] * 17:
         out = L.run(sched)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,

@@ -15,6 +15,10 @@ order + event record -> wait edges) and checks:
   5. an injected failure at any operation stops issuing, returns an error,
      leaves no wait on an unrecorded event and joins issued comm work back;
   6. both combines are ordered before the end of the compute stream.
+The receive-hook schedule (dispatch in a send phase and a receive hook run
+after one more yield, "[Core/DBO][2/N] Dual-Batch Overlap add DeepEP High
+Throughput support and Prefill support", review of modular_kernel.py) is
+checked the same way, with four yields per microbatch.
 """
 import itertools
 import os
@@ -24,10 +28,14 @@ import pytest
 
 from conftest import ROOT
 
-SCHED = {"unsplit": 0, "serial": 1, "dbo": 2, "late": 3}
-ROUTE, DISPATCH, FFN, COMBINE = range(4)
+SCHED = {"unsplit": 0, "serial": 1, "dbo": 2, "late": 3, "hook": 4}
+ROUTE, DISPATCH, FFN, COMBINE, SEND, RECV = range(6)
 COMPUTE, COMM = 0, 1
-NAMES = ["route", "dispatch", "ffn", "combine"]
+NAMES = ["route", "dispatch", "ffn", "combine", "dispatch_send", "dispatch_recv"]
+
+
+def stages_of(schedule):
+    return [ROUTE, SEND, RECV, FFN, COMBINE] if schedule == "hook" else [ROUTE, DISPATCH, FFN, COMBINE]
 
 
 @pytest.fixture(scope="module")
@@ -121,6 +129,8 @@ def accesses(mb, stage, half):
         ROUTE: ({f"x{mb}", "w_router"}, {f"{h}.logits", f"{h}.ids", f"{h}.w", f"{h}.route_ws"}),
         DISPATCH: ({f"x{mb}", f"{h}.ids"}, {f"{h}.counts", f"{h}.offsets", f"{h}.perm", f"{h}.inv",
                                            f"{h}.x_perm", f"{h}.disp_ws"}),
+        SEND: ({f"{h}.ids"}, {f"{h}.counts", f"{h}.offsets", f"{h}.perm", f"{h}.inv", f"{h}.disp_ws"}),
+        RECV: ({f"x{mb}", f"{h}.inv"}, {f"{h}.x_perm"}),
         FFN: ({f"{h}.x_perm", f"{h}.offsets", "w13", "w2", f"x{mb}", "w_shared"},
               {f"{h}.h", f"{h}.y", f"{h}.shared_h", f"{h}.shared_out"}),
         COMBINE: ({f"{h}.y", f"{h}.inv", f"{h}.w", f"{h}.shared_out"}, {f"out{mb}"}),
@@ -142,17 +152,19 @@ def races(g, halves=(0, 1)):
     return found
 
 
-@pytest.mark.parametrize("schedule", ["dbo", "late", "serial", "unsplit"])
+@pytest.mark.parametrize("schedule", ["dbo", "late", "hook", "serial", "unsplit"])
 def test_schedule_invariants(sched_bin, schedule):
     ops, status, yields = run_log(sched_bin, schedule)
     assert status == 0
     g = Graph(ops)
     assert g.wait_ok
     n_mb = 1 if schedule == "unsplit" else 2
-    stages = [ROUTE, DISPATCH, FFN, COMBINE]
+    stages = stages_of(schedule)
     assert sorted(g.launch) == sorted((mb, st) for mb in range(n_mb) for st in stages)
     if schedule in ("dbo", "late"):
         assert yields == (3, 3)
+    if schedule == "hook":
+        assert yields == (4, 4)
     # each microbatch's own chain is ordered, and the layer ends after both combines
     for mb in range(n_mb):
         chain = [g.node(mb, st) for st in stages]
@@ -174,6 +186,26 @@ def test_event_before_yield_removes_cross_microbatch_waits(sched_bin):
     assert not g.before(g.node(B, DISPATCH), g.node(A, FFN)) and not g.before(g.node(A, FFN), g.node(B, DISPATCH))
 
 
+def test_recv_hook_schedule_orders_and_overlaps(sched_bin):
+    ops, _, _ = run_log(sched_bin, "hook")
+    g = Graph(ops)
+    A, B = 0, 1
+    # the comm stream carries A.send, B.send, A.recv, B.recv, then the combines
+    comm = [(o[2], o[3]) for o in ops if o[0] == "LAUNCH" and o[1] == COMM]
+    assert comm == [(A, SEND), (B, SEND), (A, RECV), (B, RECV), (A, COMBINE), (B, COMBINE)]
+    # each microbatch's FFN waits for its own receive, not only its send
+    for mb in (A, B):
+        assert g.before(g.node(mb, RECV), g.node(mb, FFN))
+    # events before yields: A's send and combine do not wait for B's compute
+    # (A's receive runs behind B's send on the comm stream, by stream order)
+    assert not g.before(g.node(B, ROUTE), g.node(A, SEND))
+    assert g.before(g.node(B, SEND), g.node(A, RECV))
+    assert not g.before(g.node(B, FFN), g.node(A, COMBINE))
+    # and the overlaps DBO is for remain possible
+    assert not g.before(g.node(A, RECV), g.node(B, ROUTE))
+    assert not g.before(g.node(B, RECV), g.node(A, FFN)) and not g.before(g.node(A, FFN), g.node(B, RECV))
+
+
 def test_late_event_reproduces_over_serialisation(sched_bin):
     g = Graph(run_log(sched_bin, "late")[0])
     A, B = 0, 1
@@ -188,7 +220,7 @@ def test_race_detector_catches_shared_workspace(sched_bin):
     assert any("ws0.ids" in c[4] or "ws0.w" in c[4] for c in found)
 
 
-@pytest.mark.parametrize("schedule", ["dbo", "late", "serial"])
+@pytest.mark.parametrize("schedule", ["dbo", "late", "hook", "serial"])
 def test_failure_injection(sched_bin, schedule):
     full, _, _ = run_log(sched_bin, schedule)
     n_issued = sum(1 for o in full if o[0] in ("LAUNCH", "RECORD", "WAIT"))
