@@ -178,10 +178,10 @@ static moe_status launch_ffn_fp8(const FfnArgs& a, hipStream_t s) {
   p1.loc.dense_rows = a.cap_rows;
   p1.loc.g[0].n_tiles = a.I / (kF8BN / 2);
   p1.g = F8Group{static_cast<const uint8_t*>(a.x), a.xs, static_cast<const uint8_t*>(a.w13), a.s13,
-                 a.H, a.I, 2 * a.I, hq, hs};
+                 a.H, a.I, 2 * a.I, a.I / (kF8BN / 2), hq, hs};
   F8Params p2 = p1;
   p2.loc.g[0].n_tiles = a.H / kF8BN;
-  p2.g = F8Group{hq, hs, static_cast<const uint8_t*>(a.w2), a.s2, a.I, a.H, a.H, a.y, nullptr};
+  p2.g = F8Group{hq, hs, static_cast<const uint8_t*>(a.w2), a.s2, a.I, a.H, a.H, a.H / kF8BN, a.y, nullptr};
   const dim3 grid1(static_cast<unsigned>(gemm_grid(tiles_max(bm, a.cap_rows, a.E_loc, dense, p1.loc.g[0].n_tiles, 0, 0, 0))));
   const dim3 grid2(static_cast<unsigned>(gemm_grid(tiles_max(bm, a.cap_rows, a.E_loc, dense, p2.loc.g[0].n_tiles, 0, 0, 0))));
 

@@ -35,7 +35,7 @@ namespace dbomoe {
 constexpr int kF8BK = 128;          // K per stage (= bytes per row per stage)
 constexpr int kF8BN = 256;          // weight rows per column tile
 constexpr int kF8Threads = 512;     // 8 waves
-constexpr int kF8MaxK = 128 * 128;  // K blocks of a weight scale row held in two registers per lane
+constexpr int kF8MaxK = 64 * 128;   // a weight scale row (K / 128 blocks) fits one register per lane
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -50,6 +50,7 @@ struct F8Group {
   int K;                  // multiple of 128
   int N;                  // I (gate/up) or H (down)
   int b_rows;             // 2I or H
+  int n_tiles;            // column tiles (I / 128 or H / 256)
   void* C;                // gate/up: h codes [rows][N]; down: bf16 [rows][N]
   uint8_t* Cs;            // gate/up: h E8M0 bytes [rows][N / 128]
 };
@@ -104,6 +105,13 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
   const int wn = wave % S::WAVES_N;
   const int K = g.K;
   const int KT = K / kF8BK;
+  // K walked from a per-weight-tile starting stage (see the bf16 kernel): the
+  // loads and the scales of loop stage kt are those of K block stage_k(kt).
+  const int kt_rot = __builtin_amdgcn_readfirstlane(rotation_start(t.e * g.n_tiles + t.nt, KT));
+  auto stage_k = [&](int kt) {
+    const int ks = kt + kt_rot;
+    return ks >= KT ? ks - KT : ks;
+  };
   const int KB = K / 128;
   const int nt = t.nt;
 
@@ -149,26 +157,21 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
     ws1 = ws0;
   }
 
-  // The two weight scale rows, one K block per lane (lane l holds blocks l
-  // and l + 64), picked per stage with v_readlane: the K loop issues no
-  // scalar memory loads, whose completion counter the LDS reads share (a wait
-  // for an LDS read would otherwise also wait for a scale load in flight).
-  float wsv[2][2];
+  // The two weight scale rows, one K block per lane (K <= 64 blocks), picked
+  // per stage with v_readlane: the K loop issues no scalar memory loads,
+  // whose completion counter the LDS reads share (a wait for an LDS read
+  // would otherwise also wait for a scale load in flight).
+  float wsv[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float* row = j == 0 ? ws0 : ws1;
-    wsv[j][0] = row[min(lane, KB - 1)];
-    wsv[j][1] = row[min(lane + 64, KB - 1)];
-  }
-  auto wscale = [&](int j, int kt) {
-    const float v = kt < 64 ? wsv[j][0] : wsv[j][1];
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kt & 63));
+  for (int j = 0; j < 2; ++j) wsv[j] = (j == 0 ? ws0 : ws1)[min(lane, KB - 1)];
+  auto wscale = [&](int j, int kb) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wsv[j]), kb));
   };
 
   u32x4_t ra0[CA], rb0[CB], ra1[CA], rb1[CB];
   uint32_t sa0[TM], sa1[TM];
   auto load_data = [&](int kt, u32x4_t* ra, u32x4_t* rb) {
-    const uint32_t k0 = static_cast<uint32_t>(kt) * kF8BK;
+    const uint32_t k0 = static_cast<uint32_t>(stage_k(kt)) * kF8BK;
 #pragma unroll
     for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_base + (a_off[i] + k0));
 #pragma unroll
@@ -178,7 +181,7 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       const int mr = min(as_row0 + tm * 16, t.rows - 1);
-      sa[tm] = as_base[static_cast<uint32_t>(mr) * static_cast<uint32_t>(KB) + kt];
+      sa[tm] = as_base[static_cast<uint32_t>(mr) * static_cast<uint32_t>(KB) + stage_k(kt)];
     }
   };
   auto store_stage = [&](int buf, const u32x4_t* ra, const u32x4_t* rb) {
@@ -204,11 +207,12 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
                    static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
                    static_cast<int>(hi[2]), static_cast<int>(hi[3])};
   };
-  // One 16-row subtile at a time: its TN MFMAs, then their promotion into the
-  // accumulators, so at most TN products are live (the scheduling barrier
-  // keeps the compiler from hoisting the next subtile's MFMAs above them).
+  // One 16-row subtile at a time, two MFMAs at a time, each pair followed by
+  // its promotion into the accumulators, so at most two products are live
+  // (the scheduling barriers keep the compiler from hoisting later MFMAs).
   auto compute_stage = [&](int buf, const uint32_t* sa, int kt_c) {
-    const float sw[2] = {wscale(0, kt_c), wscale(1, kt_c)};
+    const int kb = stage_k(kt_c);
+    const float sw[2] = {wscale(0, kb), wscale(1, kb)};
     i32x8_t bfv[TN];
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) bfv[tn] = frag(sB[buf], f8_b_lds_row<MODE, WN, TN>(wn, tn) + frag_row);
@@ -216,14 +220,19 @@ __device__ __forceinline__ void gemm_tile_f8(const F8Group& g, const TileLoc& t,
     for (int tm = 0; tm < TM; ++tm) {
       if (tm < tm_valid) {
         const i32x8_t af = frag(sA[buf], wm * WM + tm * 16 + frag_row);
-        f32x4_t pr[TN];
+        // two MFMAs at a time, then their promotion (bounds the live products)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          pr[tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af, bfv[tn], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, static_cast<int>(sa[tm]), 0, 127);
+        for (int tn0 = 0; tn0 < TN; tn0 += 2) {
+          f32x4_t pr[2];
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] += pr[tn] * ((MODE == MODE_GATEUP && tn >= TN / 2) ? sw[1] : sw[0]);
+          for (int j = 0; j < 2; ++j)
+            pr[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af, bfv[tn0 + j], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, static_cast<int>(sa[tm]), 0, 127);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[tm][tn0 + j] += pr[j] * ((MODE == MODE_GATEUP && tn0 + j >= TN / 2) ? sw[1] : sw[0]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -233,10 +233,12 @@ def test_ffn_single_row_experts_and_gaps():
 
 
 @pytest.mark.parametrize("cid", [2, 5])
-def test_weight_streaming_kernel_matches_lds_kernel_bitwise(cid):
+def test_weight_streaming_kernel_agrees_with_lds_kernel(cid):
     """bf16: the weight-streaming kernel (16-row tiles) and the LDS-tiled kernel
-    (32-row tiles) run the same MFMA over the same K order, so their outputs
-    agree bit for bit; K = 192 and 1408-like lengths exercise the partial chunk."""
+    (32-row tiles) sum the same exact products in fp32, in different K orders
+    (the LDS-tiled kernel starts each weight tile at its own K stage), so their
+    bf16 outputs agree to a few units in the last place; K = 192 and 1408-like
+    lengths exercise the partial chunk."""
     C = _gpu()
     inp, ov = inputs(cid, True)
     cfg = inp["cfg"]
@@ -244,9 +246,15 @@ def test_weight_streaming_kernel_matches_lds_kernel_bitwise(cid):
     ref = O.dispatch_ref(ids, cfg.expert_begin, cfg.expert_end)
     x_perm = inp["x"][torch.from_numpy(ref["perm"] // cfg.k).long()].contiguous().cuda()
     off = torch.from_numpy(ref["offsets"]).cuda()
+
+    def agree(a, b, what):
+        a, b = a.float().cpu(), b.float().cpu()
+        scale = a.abs().max().item()
+        assert torch.allclose(a, b, rtol=2.0 ** -6, atol=scale * 2.0 ** -9), what
+
     ys = [_ffn(C, x_perm, cfg.I, off, cfg.E_loc, inp["w13"].cuda(), inp["w2"].cuda(), tile_m=tm)[:ref["M"]]
           for tm in (16, 32)]
-    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+    agree(ys[0], ys[1], cfg.name)
     # a long K with a partial chunk: H = 2048 (8 full chunks), I = 1408 (4 + 5 x 8 steps)
     rng = torch.Generator().manual_seed(11)
     H, I, E = 2048, 1408, 3
@@ -258,7 +266,7 @@ def test_weight_streaming_kernel_matches_lds_kernel_bitwise(cid):
     w2 = (torch.randn(E, H, I, generator=rng) * 0.02).to(torch.bfloat16).cuda()
     off = torch.from_numpy(offsets).cuda()
     ys = [_ffn(C, x, I, off, E, w13, w2, tile_m=tm) for tm in (16, 32)]
-    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+    agree(ys[0], ys[1], "H=2048 I=1408")
 
 
 @pytest.mark.parametrize("cid", CIDS)
