@@ -157,12 +157,22 @@ static int f8_tile_m(int tile_m, int64_t rows_hint) {
   return m + 3.0 * std::sqrt(m) + 1.0 <= 64 ? 64 : 128;
 }
 
+// LDS-DMA staging for K <= 4096, the register ring beyond (measured, see
+// gemm_fp8.h).
 template <int MODE>
 static void launch_f8(int bm, dim3 grid, hipStream_t s, const F8Params& p) {
-  if (bm == 128)
-    hipLaunchKernelGGL((k_gemm_f8<128, MODE>), grid, dim3(kF8Threads), 0, s, p);
-  else
-    hipLaunchKernelGGL((k_gemm_f8<64, MODE>), grid, dim3(kF8Threads), 0, s, p);
+  const bool dma = p.g.K <= kF8DmaMaxK;
+  if (bm == 128) {
+    if (dma)
+      hipLaunchKernelGGL((k_gemm_f8d<128, MODE>), grid, dim3(kF8Threads), 0, s, p);
+    else
+      hipLaunchKernelGGL((k_gemm_f8<128, MODE>), grid, dim3(kF8Threads), 0, s, p);
+  } else {
+    if (dma)
+      hipLaunchKernelGGL((k_gemm_f8d<64, MODE>), grid, dim3(kF8Threads), 0, s, p);
+    else
+      hipLaunchKernelGGL((k_gemm_f8<64, MODE>), grid, dim3(kF8Threads), 0, s, p);
+  }
 }
 
 // Routed experts through the fp8 kernel; the shared experts (weights in the
