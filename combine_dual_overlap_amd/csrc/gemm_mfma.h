@@ -37,7 +37,7 @@ namespace dbomoe {
 
 constexpr int kBK = 64;                  // K elements per LDS stage
 constexpr int kLdsStride = kBK;          // bf16 elements per LDS row (chunks XOR-swizzled)
-constexpr int kBN = 128;                 // weight rows per column tile
+constexpr int kBN = 128;                 // weight rows per column tile (32-row tiles: 64)
 
 // LDS element offset of 16-byte chunk c (8 bf16) of tile row r.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kLdsStride + ((c ^ (r & 7)) << 3); }
@@ -74,10 +74,10 @@ struct GemmParams {
                           // and output slab C + y*split_c
 };
 
-template <int BM, int WAVES_M, int WAVES_N>
+template <int BM, int WAVES_M, int WAVES_N, int BN = kBN>
 struct TileShape {
   static constexpr int WM = BM / WAVES_M;
-  static constexpr int WN = kBN / WAVES_N;
+  static constexpr int WN = BN / WAVES_N;
   static constexpr int TM = WM / 16;
   static constexpr int TN = WN / 16;
   static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
@@ -170,24 +170,25 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int* s_loc, Til
   return true;
 }
 
-// LDS row of weight tile row r -> weight row inside the expert's matrix.
-template <int MODE>
+// LDS row of weight tile row r -> weight row inside the expert's matrix
+// (tiles of BN weight rows).
+template <int MODE, int BN = kBN>
 __device__ __forceinline__ int b_global_row(const GemmGroup& g, int nt, int r) {
   if constexpr (MODE == MODE_GATEUP) {
-    return r < kBN / 2 ? nt * (kBN / 2) + r : g.N + nt * (kBN / 2) + (r - kBN / 2);
+    return r < BN / 2 ? nt * (BN / 2) + r : g.N + nt * (BN / 2) + (r - BN / 2);
   } else if constexpr (MODE == MODE_ROUTER) {
-    const int gr = nt * kBN + r;
+    const int gr = nt * BN + r;
     return gr < g.N ? gr : g.N - 1;
   } else {
-    return nt * kBN + r;
+    return nt * BN + r;
   }
 }
 
 // First LDS weight row of the wave's tn-th 16-column MFMA tile.
-template <int MODE, int WN, int TN>
+template <int MODE, int WN, int TN, int BN = kBN>
 __device__ __forceinline__ int b_lds_row(int wn, int tn) {
   if constexpr (MODE == MODE_GATEUP) {
-    return tn < TN / 2 ? wn * (WN / 2) + tn * 16 : kBN / 2 + wn * (WN / 2) + (tn - TN / 2) * 16;
+    return tn < TN / 2 ? wn * (WN / 2) + tn * 16 : BN / 2 + wn * (WN / 2) + (tn - TN / 2) * 16;
   } else {
     return wn * WN + tn * 16;
   }
@@ -224,14 +225,14 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(const u32x4_t& q, float s, u32
   hi = u32x4_t{out[4], out[5], out[6], out[7]};
 }
 
-template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8>
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8, int BN>
 __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
-                                          bf16_t (*sA)[BM * kLdsStride], bf16_t (*sB)[kBN * kLdsStride]) {
-  using S = TileShape<BM, WAVES_M, WAVES_N>;
+                                          bf16_t (*sA)[BM * kLdsStride], bf16_t (*sB)[BN * kLdsStride]) {
+  using S = TileShape<BM, WAVES_M, WAVES_N, BN>;
   constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
   constexpr int CA = BM * (kBK / 8) / 256;              // 16-byte A chunks per thread
-  constexpr int CB = FP8 ? kBN * (kBK / 16) / 256       // 16-byte B chunks per thread
-                         : kBN * (kBK / 8) / 256;
+  constexpr int CB = FP8 ? BN * (kBK / 16) / 256        // 16-byte B chunks per thread
+                         : BN * (kBK / 8) / 256;
   static_assert(CA >= 1 && CB >= 1, "chunking");
 
   const int tid = threadIdx.x;
@@ -274,8 +275,8 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
     const int c = tid + i * 256;
     const int r = FP8 ? c / (kBK / 16) : c / (kBK / 8);
     const int kc = FP8 ? c % (kBK / 16) : c % (kBK / 8);
-    const int gr = b_global_row<MODE>(g, nt, r);
-    b_up[i] = r >= kBN / 2;
+    const int gr = b_global_row<MODE, BN>(g, nt, r);
+    b_up[i] = r >= BN / 2;
     if constexpr (FP8) {
       b_src[i] = static_cast<const uint8_t*>(g.B) + static_cast<size_t>(t.e) * expert_elems +
                  static_cast<size_t>(gr) * g.ldb + ksplit + kc * 16;
@@ -296,10 +297,10 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
     const int kblocks = K / 128;
     const float* se = g.bscale + static_cast<size_t>(t.e) * (g.b_rows / 128) * kblocks;
     if constexpr (MODE == MODE_GATEUP) {
-      srow0 = se + static_cast<size_t>((nt * (kBN / 2)) / 128) * kblocks;
-      srow1 = se + static_cast<size_t>((g.N + nt * (kBN / 2)) / 128) * kblocks;
+      srow0 = se + static_cast<size_t>((nt * (BN / 2)) / 128) * kblocks;
+      srow1 = se + static_cast<size_t>((g.N + nt * (BN / 2)) / 128) * kblocks;
     } else {
-      srow0 = se + static_cast<size_t>((nt * kBN) / 128) * kblocks;
+      srow0 = se + static_cast<size_t>((nt * BN) / 128) * kblocks;
       srow1 = srow0;
     }
   }
@@ -382,7 +383,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
         bfv[tn] = *reinterpret_cast<const bf16x8_t*>(
-            &sB[buf][lds_off(b_lds_row<MODE, WN, TN>(wn, tn) + frag_row, kk * 4 + frag_c)]);
+            &sB[buf][lds_off(b_lds_row<MODE, WN, TN, BN>(wn, tn) + frag_row, kk * 4 + frag_c)]);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
         if (tm < tm_valid)
@@ -445,7 +446,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < TN / 2; ++tn) {
-        const int col = nt * (kBN / 2) + wn * (WN / 2) + tn * 16 + col_in;
+        const int col = nt * (BN / 2) + wn * (WN / 2) + tn * 16 + col_in;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
@@ -462,7 +463,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const int col = nt * kBN + wn * WN + tn * 16 + col_in;
+        const int col = nt * BN + wn * WN + tn * 16 + col_in;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
@@ -475,7 +476,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const int col = nt * kBN + wn * WN + tn * 16 + col_in;
+        const int col = nt * BN + wn * WN + tn * 16 + col_in;
         if (col < g.N) {
           const float b = p.bias ? p.bias[col] : 0.f;
 #pragma unroll
@@ -492,18 +493,18 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
 // LDS, so four workgroups share a CU), 3 for 64 rows, 2 for 128 rows.
 template <int BM> struct MinWaves { static constexpr int value = BM == 32 ? 4 : BM == 64 ? 3 : 2; };
 
-template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8>
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8, int BN = kBN>
 __global__ __launch_bounds__(256, MinWaves<BM>::value) void k_gemm_nt(GemmParams p) {
   __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kBN * kLdsStride];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * kLdsStride];
   int* s_loc = reinterpret_cast<int*>(&sA[0][0]);   // tile location, before sA holds A tiles
   TileLoc t;
   if (!locate_tile<BM>(p, s_loc, t)) return;
   __syncthreads();                                  // s_loc read by all before sA is filled
   if (FP8 && t.grp == 0)
-    gemm_tile<BM, WAVES_M, WAVES_N, MODE, FP8>(p.g[0], t, p, sA, sB);
+    gemm_tile<BM, WAVES_M, WAVES_N, MODE, FP8, BN>(p.g[0], t, p, sA, sB);
   else
-    gemm_tile<BM, WAVES_M, WAVES_N, MODE, false>(p.g[t.grp], t, p, sA, sB);
+    gemm_tile<BM, WAVES_M, WAVES_N, MODE, false, BN>(p.g[t.grp], t, p, sA, sB);
 }
 
 // Worst-case number of row tiles: sum_e ceil(n_e / BM) <= ceil(cap / BM) + E_loc.
