@@ -25,6 +25,10 @@
 //  * Operand lanes: lane l holds row (or weight row) l % 16 and the 32 bytes
 //    [32 (l / 16), 32 (l / 16) + 32) of the stage's K block.  A and B use the
 //    same K assignment, so every product pairs matching K indices.
+//  * Two stagings of the same arithmetic: k_gemm_f8 moves each stage through a
+//    two-deep register ring into double-buffered LDS; k_gemm_f8d (further down)
+//    loads straight into three LDS stages with LDS DMA.  The host takes the
+//    DMA variant for K <= 4096.
 #pragma once
 
 #include "fp8_act.h"
@@ -371,7 +375,8 @@ __global__ __launch_bounds__(kF8Threads, 2) void k_gemm_f8(F8Params p) {
 // lane l's bytes land at LDS address lds_addr + 16 l.  Issued as inline
 // assembly so that the compiler does not wait for every such load before each
 // LDS read (it cannot tell the three stage buffers apart); the kernel counts
-// them itself with s_waitcnt.
+// them itself with s_waitcnt.  The assembly sets M0, which the compiler does
+// not use anywhere in these kernels (checked in the generated code).
 __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gptr) {
   const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(gptr) : "memory");
