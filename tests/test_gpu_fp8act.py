@@ -202,6 +202,32 @@ def test_grouped_ffn_fp8_ragged_experts():
         assert_close(to_f64(y), want, TOL, f"ragged fp8-act tile_m={tm}", scale)
 
 
+def test_grouped_ffn_fp8_long_k_register_ring_kernel():
+    """K > 4096 in both GEMMs (H = 4352, I = 4224): the register-ring staging
+    runs instead of the LDS-DMA one, for both row tiles."""
+    B = _B()
+    g = torch.Generator().manual_seed(12)
+    H, I = 4352, 4224
+    counts = np.array([3, 70])
+    E = counts.size
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offsets[-1])
+    x = torch.randn(M, H, generator=g).to(torch.bfloat16)
+    w13c, s13 = zip(*[W.quantize_fp8_blocks(torch.randn(2 * I, H, generator=g) * 0.02) for _ in range(E)])
+    w2c, s2 = zip(*[W.quantize_fp8_blocks(torch.randn(H, I, generator=g) * 0.02) for _ in range(E)])
+    w13c, s13, w2c, s2 = (torch.stack(t).contiguous() for t in (w13c, s13, w2c, s2))
+    xq = torch.empty(M, H, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(M, H // 128, dtype=torch.uint8, device="cuda")
+    B.moe_quant_fp8_rows(x.cuda(), xq, xs)
+    wof = lambda e: (O.dequant_fp8_blocks(w13c[e].numpy(), s13[e].numpy()),
+                     O.dequant_fp8_blocks(w2c[e].numpy(), s2[e].numpy()))
+    want, scale = O.grouped_ffn_fp8act_ref(O.decode(W.bits(x), "bf16"), offsets, wof, with_scale=True)
+    for tm in (64, 128):
+        y = _ffn_fp8(B, xq, xs, I, torch.from_numpy(offsets).cuda(), E, w13c.cuda(), w2c.cuda(), s13.cuda(),
+                     s2.cuda(), tm)
+        assert_close(to_f64(y), want, TOL, f"long K fp8-act tile_m={tm}", scale)
+
+
 def test_grouped_ffn_fp8_rejects_bad_shapes():
     B = _B()
     d = lambda *s: torch.zeros(*s, dtype=torch.uint8, device="cuda")
