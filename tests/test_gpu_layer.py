@@ -179,20 +179,22 @@ def test_timing_events_report_ffn_times():
     assert L.ctx.ffn_times() == t2            # untimed calls leave the record alone
 
 
-@pytest.mark.parametrize("cid", [2, 3, 5])
-@pytest.mark.parametrize("schedule", ["dbo", "serial"])
-def test_layer_captured_in_a_graph_replays_exactly(cid, schedule):
+@pytest.mark.parametrize("cid,fp8_act", [(2, False), (3, False), (5, False), (3, True), (4, True)])
+@pytest.mark.parametrize("schedule", ["dbo", "serial", "dbo_recv_hook"])
+def test_layer_captured_in_a_graph_replays_exactly(cid, fp8_act, schedule):
     """dbo_moe_layer under stream capture (the comm stream joins the capture
     through the layer's events; device-side counts, no host sync): every
     replay, with eager layer calls in between, equals the eager output bit for
-    bit, and the eager output is within tolerance of the oracle."""
+    bit, and the eager output is within tolerance of the oracle (bf16 and fp8
+    activations, every two-microbatch schedule)."""
     inp, ov = inputs(cid, True)
     cfg = inp["cfg"]
-    L = _layer(inp)
+    L = _layer(inp, fp8_act=fp8_act)
     eager = L.run(schedule).clone()
     torch.cuda.synchronize()
-    ref = O.moe_layer_expert(ov)
-    print(f"graph cfg={cfg.name} schedule={schedule}", flush=True)
+    ids = _gpu_routing(L, cfg, ov, (cfg.T + 1) // 2)
+    ref = _reference(dict(ov, fp8_act=fp8_act), ids)
+    print(f"graph cfg={cfg.name} fp8_act={fp8_act} schedule={schedule}", flush=True)
     assert_close(to_f64(eager), ref["out"], tol_for(cfg), "eager", ref["scale"])
     out = torch.empty_like(L.out)
     side = torch.cuda.Stream()
