@@ -35,13 +35,23 @@ static int choose_tile_m(int64_t mean_rows) {
 // The 32-row tile takes 64 weight rows per column tile (2 x 2 waves of 16 x
 // 32): twice the tiles of 128-row-wide columns, so the last partial round of
 // workgroups is shorter (decode gate/up with the shared experts 145.5 ->
-// 140.9 us, down 75.0 -> 73.1 us, standalone).
+// 140.9 us, down 75.0 -> 73.1 us, standalone).  When K allows, it stages K
+// 128 wide (256 contiguous bytes of each weight row per stage, three
+// workgroups per CU): decode gate/up 146.0 -> 144.4 us in the layer; 256
+// wide (one workgroup per CU) was slower, 168.8 us.
 static int col_tile_rows(int bm) { return bm == 32 ? 64 : kBN; }
+
+// True if every group of the launch has a K that is a multiple of bk.
+static bool k_multiple_of(const GemmParams& g, int bk) {
+  return g.g[0].K % bk == 0 && (g.rows1 == 0 || g.g[1].K % bk == 0);
+}
 
 template <int MODE, bool FP8>
 static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g) {
   if (bm == 16)
     hipLaunchKernelGGL((k_gemm_ws<MODE, FP8>), grid, dim3(kWsWaves * kWave), 0, s, g);
+  else if (bm == 32 && k_multiple_of(g, 2 * kBK))
+    hipLaunchKernelGGL((k_gemm_nt<32, 2, 2, MODE, FP8, 64, 2 * kBK>), grid, dim3(256), 0, s, g);
   else if (bm == 32)
     hipLaunchKernelGGL((k_gemm_nt<32, 2, 2, MODE, FP8, 64>), grid, dim3(256), 0, s, g);
   else if (bm == 64)

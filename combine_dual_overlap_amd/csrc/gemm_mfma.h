@@ -20,14 +20,15 @@
 //    column tile come first, then the next column tile, so row tiles that share
 //    a weight tile run at the same time on one XCD and read it through its L2.
 //  * 4 waves; each wave owns a WM x WN block made of 16x16 MFMA tiles
-//    (v_mfma_f32_16x16x32_bf16, fp32 accumulators).  K advances 64 per stage.
+//    (v_mfma_f32_16x16x32_bf16, fp32 accumulators).  K advances BK per stage
+//    (64; 128 for the 32-row decode tile when K allows).
 //    Global loads run two stages ahead of the MFMAs (a two-deep register ring)
 //    and land in a double-buffered LDS tile (one barrier per stage).  LDS rows
 //    are 128 bytes with the 16-byte chunks XOR-swizzled by row, so the 16 rows
 //    an MFMA fragment read touches fall in distinct banks without padding (the
 //    32-row tile then fits four workgroups per CU).
 //  * fp8 e4m3 weights are expanded on their way to LDS: code value times its
-//    128x128 block scale, rounded once to bf16 (the stage's 64-wide K slice lies
+//    128x128 block scale, rounded once to bf16 (the stage's 64- or 128-wide K slice lies
 //    in one scale block, and so do the 64 gate or 64 up rows of a tile).
 #pragma once
 
@@ -40,7 +41,10 @@ constexpr int kLdsStride = kBK;          // bf16 elements per LDS row (chunks XO
 constexpr int kBN = 128;                 // weight rows per column tile (32-row tiles: 64)
 
 // LDS element offset of 16-byte chunk c (8 bf16) of tile row r.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * kLdsStride + ((c ^ (r & 7)) << 3); }
+// With BK-wide stages the rows are BK elements long; the swizzle is the same.
+template <int BK>
+__device__ __forceinline__ int lds_off_k(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+__device__ __forceinline__ int lds_off(int r, int c) { return lds_off_k<kLdsStride>(r, c); }
 
 enum GemmMode { MODE_ROUTER = 0, MODE_GATEUP = 1, MODE_DOWN = 2 };
 
@@ -225,15 +229,16 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(const u32x4_t& q, float s, u32
   hi = u32x4_t{out[4], out[5], out[6], out[7]};
 }
 
-template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8, int BN>
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8, int BN, int BK>
 __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
-                                          bf16_t (*sA)[BM * kLdsStride], bf16_t (*sB)[BN * kLdsStride]) {
+                                          bf16_t (*sA)[BM * BK], bf16_t (*sB)[BN * BK]) {
   using S = TileShape<BM, WAVES_M, WAVES_N, BN>;
   constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
-  constexpr int CA = BM * (kBK / 8) / 256;              // 16-byte A chunks per thread
-  constexpr int CB = FP8 ? BN * (kBK / 16) / 256        // 16-byte B chunks per thread
-                         : BN * (kBK / 8) / 256;
+  constexpr int CA = BM * (BK / 8) / 256;              // 16-byte A chunks per thread
+  constexpr int CB = FP8 ? BN * (BK / 16) / 256        // 16-byte B chunks per thread
+                         : BN * (BK / 8) / 256;
   static_assert(CA >= 1 && CB >= 1, "chunking");
+  static_assert(!FP8 || 128 % BK == 0, "an fp8 stage must lie inside one 128-wide scale block");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,7 +246,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   const int K = g.K;
-  const int KT = K / kBK;
+  const int KT = K / BK;
   // With 32-row tiles (decode: the GEMM streams weights) each column tile
   // walks K from its own starting stage, wrapping around: tiles that stream
   // their weights at the same K offset at the same time hit the same HBM
@@ -259,12 +264,12 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
     const int c = tid + i * 256;
-    const int r = c / (kBK / 8);
-    const int kc = c % (kBK / 8);
+    const int r = c / (BK / 8);
+    const int kc = c % (BK / 8);
     int mr = t.m_off + r;
     mr = mr < t.rows ? mr : t.rows - 1;
     a_src[i] = g.A + t.e * g.a_estride + (t.row_begin + mr) * g.lda + ksplit + kc * 8;
-    a_lds[i] = lds_off(r, kc);
+    a_lds[i] = lds_off_k<BK>(r, kc);
   }
   const size_t expert_elems = static_cast<size_t>(g.b_estride);
   const uint8_t* b_src[CB];
@@ -273,20 +278,20 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int c = tid + i * 256;
-    const int r = FP8 ? c / (kBK / 16) : c / (kBK / 8);
-    const int kc = FP8 ? c % (kBK / 16) : c % (kBK / 8);
+    const int r = FP8 ? c / (BK / 16) : c / (BK / 8);
+    const int kc = FP8 ? c % (BK / 16) : c % (BK / 8);
     const int gr = b_global_row<MODE, BN>(g, nt, r);
     b_up[i] = r >= BN / 2;
     if constexpr (FP8) {
       b_src[i] = static_cast<const uint8_t*>(g.B) + static_cast<size_t>(t.e) * expert_elems +
                  static_cast<size_t>(gr) * g.ldb + ksplit + kc * 16;
-      b_lds[i] = lds_off(r, 2 * kc);          // 16 fp8 codes -> two 8-element bf16 chunks
-      b_lds2[i] = lds_off(r, 2 * kc + 1);
+      b_lds[i] = lds_off_k<BK>(r, 2 * kc);          // 16 fp8 codes -> two 8-element bf16 chunks
+      b_lds2[i] = lds_off_k<BK>(r, 2 * kc + 1);
     } else {
       b_src[i] = reinterpret_cast<const uint8_t*>(static_cast<const bf16_t*>(g.B) +
                                                   static_cast<size_t>(t.e) * expert_elems +
                                                   static_cast<size_t>(gr) * g.ldb + ksplit + kc * 8);
-      b_lds[i] = lds_off(r, kc);
+      b_lds[i] = lds_off_k<BK>(r, kc);
       b_lds2[i] = b_lds[i];
     }
   }
@@ -325,7 +330,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
   auto load_stage = [&](int kt, u32x4_t* ra, u32x4_t* rb, float* sc) {
     int ks = kt + kt_rot;
     ks = ks >= KT ? ks - KT : ks;
-    const int k0 = ks * kBK;
+    const int k0 = ks * BK;
 #pragma unroll
     for (int i = 0; i < CA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + k0);
 #pragma unroll
@@ -373,17 +378,17 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
       max(0, min(TM, (t.rows - t.m_off - wm * WM + 15) / 16)));
   auto compute_stage = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
+    for (int kk = 0; kk < BK / 32; ++kk) {
       bf16x8_t af[TM], bfv[TN];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
         if (tm < tm_valid)
           af[tm] = *reinterpret_cast<const bf16x8_t*>(
-              &sA[buf][lds_off(wm * WM + tm * 16 + frag_row, kk * 4 + frag_c)]);
+              &sA[buf][lds_off_k<BK>(wm * WM + tm * 16 + frag_row, kk * 4 + frag_c)]);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
         bfv[tn] = *reinterpret_cast<const bf16x8_t*>(
-            &sB[buf][lds_off(b_lds_row<MODE, WN, TN, BN>(wn, tn) + frag_row, kk * 4 + frag_c)]);
+            &sB[buf][lds_off_k<BK>(b_lds_row<MODE, WN, TN, BN>(wn, tn) + frag_row, kk * 4 + frag_c)]);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
         if (tm < tm_valid)
@@ -489,22 +494,25 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
   }
 }
 
-// Waves per SIMD each tile shape is built for: 4 for the 32-row tile (40 KB of
-// LDS, so four workgroups share a CU), 3 for 64 rows, 2 for 128 rows.
-template <int BM> struct MinWaves { static constexpr int value = BM == 32 ? 4 : BM == 64 ? 3 : 2; };
+// Waves per SIMD each tile shape is built for: 4 for the 32-row tile with
+// 64-wide K stages (24 KB of LDS), 3 with 128-wide stages (48 KB: three
+// workgroups share a CU), 3 for 64 rows, 2 for 128 rows.
+template <int BM, int BK> struct MinWaves {
+  static constexpr int value = BM == 32 ? (BK == 64 ? 4 : 3) : BM == 64 ? 3 : 2;
+};
 
-template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8, int BN = kBN>
-__global__ __launch_bounds__(256, MinWaves<BM>::value) void k_gemm_nt(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * kLdsStride];
+template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8, int BN = kBN, int BK = kBK>
+__global__ __launch_bounds__(256, (MinWaves<BM, BK>::value)) void k_gemm_nt(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * BK];
   int* s_loc = reinterpret_cast<int*>(&sA[0][0]);   // tile location, before sA holds A tiles
   TileLoc t;
   if (!locate_tile<BM>(p, s_loc, t)) return;
   __syncthreads();                                  // s_loc read by all before sA is filled
   if (FP8 && t.grp == 0)
-    gemm_tile<BM, WAVES_M, WAVES_N, MODE, FP8, BN>(p.g[0], t, p, sA, sB);
+    gemm_tile<BM, WAVES_M, WAVES_N, MODE, FP8, BN, BK>(p.g[0], t, p, sA, sB);
   else
-    gemm_tile<BM, WAVES_M, WAVES_N, MODE, false, BN>(p.g[t.grp], t, p, sA, sB);
+    gemm_tile<BM, WAVES_M, WAVES_N, MODE, false, BN, BK>(p.g[t.grp], t, p, sA, sB);
 }
 
 // Worst-case number of row tiles: sum_e ceil(n_e / BM) <= ceil(cap / BM) + E_loc.
