@@ -124,7 +124,49 @@ def comm_work(cfg, L, halves, comm_ms, fp8_act=False):
         gbs = float(np.mean(byts)) / avg_s / 1e9
         out[name] = {"avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": int(np.mean(byts)),
                      "achieved_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    if not fp8_act:
+        out["dispatch"]["row_gather_kernel"], out["combine"]["kernel_without_shared"] = \
+            comm_kernels_alone(cfg, L, halves[0])
     return out
+
+
+def comm_kernels_alone(cfg, L, half, reps=20):
+    """The data-moving kernels of the comm steps timed alone (HIP events
+    around `reps` back-to-back calls on the current stream), on microbatch 0's
+    routing: the row gather of the dispatch (moe_dispatch_recv; its count and
+    rank kernels excluded) and the combine without the shared-expert slabs."""
+    import torch
+    from combine_dual_overlap_amd import binding as B
+    a, b = half
+    n = b - a
+    s = 4 if cfg.act == "f32" else 2
+    x = L.x[a:b]
+    inv = L.view(0, "inv", torch.int32, (n * cfg.k,), T=cfg.T)
+    w = L.view(0, "topk_w", torch.float32, (n, cfg.k), T=cfg.T)
+    inv_np = inv.cpu().numpy().reshape(n, cfg.k)
+    M = int((inv_np >= 0).sum())
+    t_hit = int((inv_np >= 0).any(axis=1).sum())
+    rows = torch.empty(max(n * cfg.k, 1), cfg.H, dtype=x.dtype, device=x.device)
+    out = torch.empty(n, cfg.H, dtype=x.dtype, device=x.device)
+    calls = {"gather": lambda: B.moe_dispatch_recv(x, cfg.k, inv, rows),
+             "combine": lambda: B.moe_combine(rows, n, cfg.k, inv, w, out)}
+    byts = {"gather": t_hit * cfg.H * s + M * cfg.H * s + 4 * n * cfg.k,
+            "combine": M * cfg.H * s + 8 * n * cfg.k + n * cfg.H * s}
+    rec = []
+    for name in ("gather", "combine"):
+        for _ in range(3):
+            calls[name]()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            calls[name]()
+        t1.record()
+        torch.cuda.synchronize()
+        avg_s = t0.elapsed_time(t1) / reps / 1e3
+        gbs = byts[name] / avg_s / 1e9
+        rec.append({"avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": int(byts[name]),
+                    "achieved_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+    return rec
 
 
 def cpu_baseline(inp, cfg, budget_s: float, fp8_act=False):

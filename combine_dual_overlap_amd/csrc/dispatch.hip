@@ -7,8 +7,12 @@
 // rows ("DeepEP HT: full decode CUDA graphs via worst-token dispatch", bot
 // review 2), so nothing waits on the host.
 //
-// Four kernels, each a pass over HBM-resident data (small batches fuse the
-// first three into one workgroup, k_disp_small):
+// Four kernels, each a pass over HBM-resident data.  Small batches fuse the
+// first three into one workgroup (k_disp_small); mid-sized batches (up to
+// 256 local experts and 64k block-histogram entries, i.e. the prefill
+// microbatches) count 1024 pairs per workgroup and fold the scan into the rank
+// kernel (k_disp_rank_scan: every workgroup sums the histograms of the blocks
+// before it and scans the expert totals itself), so they take three launches:
 //  1. count   - one workgroup per 256 pairs: LDS histogram of local experts;
 //               flags ids outside [0, E).
 //  2. scan    - one workgroup: per expert, exclusive prefix over the blocks
@@ -59,14 +63,16 @@ static DispWs carve(void* ws, int64_t nb, int32_t E_loc) {
   return d;
 }
 
-__global__ __launch_bounds__(256) void k_disp_count(const int32_t* __restrict__ ids, int64_t n_pairs,
+// One pair per thread, PPB pairs per workgroup.
+template <int PPB>
+__global__ __launch_bounds__(PPB) void k_disp_count(const int32_t* __restrict__ ids, int64_t n_pairs,
                                                     int E_total, int e_begin, int E_loc,
                                                     int32_t* __restrict__ block_hist,
                                                     int32_t* __restrict__ block_err) {
   __shared__ int hist[kMaxELoc];
-  for (int e = threadIdx.x; e < E_loc; e += 256) hist[e] = 0;
+  for (int e = threadIdx.x; e < E_loc; e += PPB) hist[e] = 0;
   __syncthreads();
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * kPairsPerBlock + threadIdx.x;
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * PPB + threadIdx.x;
   int bad = 0;
   if (p < n_pairs) {
     const int e = ids[p];
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(256) void k_disp_count(const int32_t* __restrict__ 
   }
   bad = __syncthreads_or(bad);
   int32_t* out = block_hist + static_cast<int64_t>(blockIdx.x) * E_loc;
-  for (int e = threadIdx.x; e < E_loc; e += 256) out[e] = hist[e];
+  for (int e = threadIdx.x; e < E_loc; e += PPB) out[e] = hist[e];
   if (threadIdx.x == 0) block_err[blockIdx.x] = bad;
 }
 
@@ -203,13 +209,122 @@ __global__ __launch_bounds__(256) void k_disp_rank(const int32_t* __restrict__ i
   }
 }
 
+// Mid-sized batches: 1024 pairs per workgroup for both the count and this
+// kernel.  Workgroup b first sums the block histograms: thread (e, part) adds
+// a run of blocks of expert column e (loads coalesced across experts), split
+// into the blocks before b (b's stable base inside each expert) and all blocks
+// (the expert totals).  Every workgroup then scans the totals into offsets
+// itself (no scan launch); workgroup 0 writes counts, offsets, tile offsets
+// and the error word.  The ranks of b's 1024 pairs follow as in k_disp_small.
+constexpr int kMidPairsPerBlock = 1024;
+constexpr int kMidMaxELoc = 256;
+constexpr int64_t kMidMaxHist = 65536;    // blocks x local experts summed by each workgroup
+
+__global__ __launch_bounds__(1024) void k_disp_rank_scan(const int32_t* __restrict__ ids, int64_t n_pairs,
+                                                         int e_begin, int E_loc, int64_t nb, int parts,
+                                                         int tile_m, const int32_t* __restrict__ block_hist,
+                                                         const int32_t* __restrict__ block_err,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ tile_offsets,
+                                                         int32_t* __restrict__ err,
+                                                         int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int s_pre[kMidMaxELoc];        // pairs of expert e in blocks before this one
+  __shared__ int s_tot[kMidMaxELoc];        // pairs of expert e in all blocks, then the running position
+  __shared__ int s_wcnt[16][kMidMaxELoc];   // this block's count per wave and expert
+  __shared__ int s_wsum[32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t b = blockIdx.x;
+  for (int e = tid; e < E_loc; e += 1024) {
+    s_pre[e] = 0;
+    s_tot[e] = 0;
+  }
+  for (int i = tid; i < 16 * E_loc; i += 1024) s_wcnt[i / E_loc][i % E_loc] = 0;
+  __syncthreads();
+  if (tid < parts * E_loc) {
+    const int e = tid % E_loc;
+    const int part = tid / E_loc;
+    const int64_t per = (nb + parts - 1) / parts;
+    const int64_t r0 = min(nb, part * per);
+    const int64_t r1 = min(nb, r0 + per);
+    constexpr int U = 16;
+    int pre = 0, tot = 0;
+    for (int64_t r = r0; r < r1; r += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = r + u < r1 ? block_hist[(r + u) * E_loc + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        tot += v[u];
+        pre += r + u < b ? v[u] : 0;
+      }
+    }
+    if (pre) atomicAdd(&s_pre[e], pre);
+    if (tot) atomicAdd(&s_tot[e], tot);
+  }
+  int any = 0;
+  if (b == 0)
+    for (int64_t q = tid; q < nb; q += 1024) any |= block_err[q];
+  any = __syncthreads_or(any);
+  const int cnt = tid < E_loc ? s_tot[tid] : 0;
+  const int off = block_excl_scan_1024(cnt, s_wsum);
+  if (b == 0) {
+    if (tid < E_loc) {
+      counts[tid] = cnt;
+      offsets[tid] = off;
+    }
+    if (tid == E_loc - 1) offsets[E_loc] = off + cnt;
+    if (tid == 0) err[0] = any;
+  }
+  if (tile_offsets) {
+    const int tiles = (cnt + tile_m - 1) / tile_m;
+    const int toff = block_excl_scan_1024(tiles, s_wsum);
+    if (b == 0) {
+      if (tid < E_loc) tile_offsets[tid] = toff;
+      if (tid == E_loc - 1) tile_offsets[E_loc] = toff + tiles;
+    }
+  }
+  if (tid < E_loc) s_tot[tid] = off + s_pre[tid];
+  // ranks of this block's pairs: ballot groups per wave, then the lower waves
+  const int64_t p = b * kMidPairsPerBlock + tid;
+  int le = -1;
+  if (p < n_pairs) {
+    const int e = ids[p] - e_begin;
+    if (e >= 0 && e < E_loc) le = e;
+  }
+  const bool local = le >= 0;
+  uint64_t remaining = __ballot(local);
+  uint64_t mine = 0;
+  while (remaining) {
+    const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+    const int lead_e = __shfl(le, leader, kWave);
+    const uint64_t m = __ballot(local && le == lead_e);
+    if (local && le == lead_e) mine = m;
+    remaining &= ~m;
+  }
+  const uint64_t lower = mine & lanemask_lt();
+  if (local && lower == 0) s_wcnt[wave][le] = __popcll(mine);
+  __syncthreads();
+  if (p < n_pairs) {
+    int pos = -1;
+    if (local) {
+      pos = s_tot[le] + __popcll(lower);
+      for (int w = 0; w < wave; ++w) pos += s_wcnt[w][le];
+      perm[pos] = static_cast<int32_t>(p);
+    }
+    inv[p] = pos;
+  }
+  (void)lane;
+}
+
 // Small batches (few pairs, E_loc <= 256): count, scan and rank in one
 // workgroup, so the dispatch is two launches (this and the gather) instead of
 // four.  Pairs are taken 1024 at a time in order; inside a chunk a pair's
 // stable rank is its rank among same-expert lanes of its wave (ballot groups)
 // plus the counts of the lower waves, on top of the expert's running count.
 constexpr int kSmallChunk = 1024;
-constexpr int kSmallMaxPairs = 8192;
+constexpr int kSmallMaxPairs = 2048;
 constexpr int kSmallMaxELoc = 256;
 
 __global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__ ids, int64_t n_pairs,
@@ -409,9 +524,22 @@ moe_status launch_dispatch_send(const DispatchArgs& a, hipStream_t s) {
     DBOMOE_CHECK_LAUNCH();
     return MOE_OK;
   }
+  const int64_t nb_mid = (n_pairs + kMidPairsPerBlock - 1) / kMidPairsPerBlock;
+  if (E_loc <= kMidMaxELoc && nb_mid * E_loc <= kMidMaxHist) {
+    hipLaunchKernelGGL(k_disp_count<kMidPairsPerBlock>, dim3(static_cast<unsigned>(nb_mid)),
+                       dim3(kMidPairsPerBlock), 0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist,
+                       w.block_err);
+    DBOMOE_CHECK_LAUNCH();
+    const int parts = static_cast<int>(std::min<int64_t>(std::max(1, 1024 / E_loc), nb_mid));
+    hipLaunchKernelGGL(k_disp_rank_scan, dim3(static_cast<unsigned>(nb_mid)), dim3(1024), 0, s, a.ids, n_pairs,
+                       a.e_begin, E_loc, nb_mid, parts, a.tile_m > 0 ? a.tile_m : 1, w.block_hist, w.block_err,
+                       a.counts, a.offsets, a.tile_m > 0 ? a.tile_offsets : nullptr, w.err, a.perm, a.inv);
+    DBOMOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
   if (nb > 0) {
-    hipLaunchKernelGGL(k_disp_count, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, a.ids, n_pairs,
-                       a.E_total, a.e_begin, E_loc, w.block_hist, w.block_err);
+    hipLaunchKernelGGL(k_disp_count<kPairsPerBlock>, dim3(static_cast<unsigned>(nb)), dim3(kPairsPerBlock), 0, s,
+                       a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist, w.block_err);
     DBOMOE_CHECK_LAUNCH();
   }
   int tpe = 1;

@@ -122,12 +122,19 @@ def test_dispatch(cid, small):
         assert C.binding.moe_get_device_error(g["ws"]) == 0
 
 
-# Up to 8192 pairs and 256 local experts the dispatch runs its one-workgroup
-# count/scan/rank kernel (pairs taken 1024 at a time); beyond, four kernels.
-@pytest.mark.parametrize("T,k,E,lo,hi", [(1, 1, 1, 0, 1), (3, 2, 5, 1, 4), (300, 8, 256, 0, 32),
-                                         (257, 6, 64, 0, 64), (64, 16, 300, 100, 300),
+# Three dispatch paths: up to 2048 pairs and 256 local experts one workgroup
+# counts, scans and ranks (pairs taken 1024 at a time); up to 256 local experts
+# and 65536 entries of 1024-pair block histograms, a count kernel and a rank
+# kernel that scans for itself; beyond, count, scan and rank kernels over
+# 256-pair blocks.  The shapes below cover each path, partial last blocks,
+# one local expert, non-local pairs and the boundaries between the paths.
+@pytest.mark.parametrize("T,k,E,lo,hi", [(1, 1, 1, 0, 1), (3, 2, 5, 1, 4), (257, 6, 64, 0, 64),
+                                         (64, 16, 300, 100, 300), (256, 8, 64, 0, 64),
+                                         (2049, 1, 8, 0, 8), (300, 8, 256, 0, 32), (5000, 1, 1, 0, 1),
                                          (1024, 8, 64, 0, 64), (1025, 8, 64, 0, 64),
-                                         (2048, 4, 256, 0, 256), (1000, 3, 300, 0, 257)])
+                                         (2048, 4, 256, 0, 256), (3000, 8, 256, 32, 64),
+                                         (8193, 8, 64, 0, 64), (1000, 3, 300, 0, 257),
+                                         (33000, 8, 256, 0, 256)])
 @pytest.mark.parametrize("two_phase", [False, True])
 def test_dispatch_shapes(T, k, E, lo, hi, two_phase):
     C = _gpu()
@@ -149,18 +156,29 @@ def test_dispatch_all_to_one_expert_and_repeats():
     _check_dispatch(cfg, x, ids, g)
 
 
-def test_dispatch_flags_bad_ids():
+@pytest.mark.parametrize("T,E", [(10, 8), (1500, 8), (4000, 300)])     # each dispatch path
+def test_dispatch_flags_bad_ids(T, E):
     C = _gpu()
-    cfg = W.LayerConfig("bad", T=10, H=128, E=8, k=2, I=64, act="bf16", wdt="bf16")
-    ids = np.tile(np.array([[1, 2]], np.int32), (10, 1))
-    ids[4, 1] = 8
-    ids[7, 0] = -1
-    x = torch.randn(10, 128).to(torch.bfloat16)
+    cfg = W.LayerConfig("bad", T=T, H=128, E=E, k=2, I=64, act="bf16", wdt="bf16")
+    ids = np.tile(np.array([[1, 2]], np.int32), (T, 1))
+    bad = [(4, 1, E), (7, 0, -1), (T - 1, 1, 1 << 20)]
+    for t, j, v in bad:
+        ids[t, j] = v
+    x = torch.randn(T, 128).to(torch.bfloat16)
     g = _dispatch(C, cfg, x.cuda(), torch.from_numpy(ids).cuda())
     assert C.binding.moe_get_device_error(g["ws"]) == 1
     inv = g["inv"].cpu().numpy()
-    assert inv[4 * 2 + 1] == -1 and inv[7 * 2 + 0] == -1
-    assert g["offsets"].cpu().numpy()[-1] == 18
+    assert all(inv[t * 2 + j] == -1 for t, j, _ in bad)
+    assert g["offsets"].cpu().numpy()[-1] == 2 * T - len(bad)
+    good = ids.copy()
+    for t, j, _ in bad:
+        good[t, j] = 0          # a valid id that the check below leaves out
+    ref = O.dispatch_ref(good, 0, E)
+    keep = np.ones(2 * T, bool)
+    keep[[t * 2 + j for t, j, _ in bad]] = False
+    # the valid pairs keep their order: perm lists them by (expert, pair index)
+    want = ref["perm"][keep[ref["perm"]]]
+    assert np.array_equal(g["perm"].cpu().numpy()[:2 * T - len(bad)], want)
 
 
 def test_dispatch_empty_batch():
