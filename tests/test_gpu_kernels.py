@@ -232,10 +232,11 @@ def test_dense_shared_ffn():
     assert_close(to_f64(y), sum(p[0] for p in parts), 1e-2, "shared expert", sum(p[1] for p in parts))
 
 
-def test_ffn_single_row_experts_and_gaps():
+# One column tile and several; an I that is not a multiple of 128.
+@pytest.mark.parametrize("H,I", [(256, 128), (512, 384), (256, 192)])
+def test_ffn_single_row_experts_and_gaps(H, I):
     C = _gpu()
-    rng = np.random.default_rng(7)
-    H, I, E = 256, 128, 6
+    E = 6
     counts = np.array([1, 0, 33, 0, 129, 2])
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     M = int(offsets[-1])
