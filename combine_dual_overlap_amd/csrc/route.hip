@@ -59,32 +59,15 @@ __device__ __forceinline__ void wave_argmax(float& v, int& e) {
   }
 }
 
-constexpr int kMaxK = 16;
 
-// One wave per token, 4 tokens per workgroup.  Lane l holds experts l, l+64, ...
-__global__ __launch_bounds__(256) void k_topk(TopkParams p) {
-  __shared__ float s_score[4][256];
+// Selection and weights of token t, one wave: lane l holds the logits of
+// experts l, l+64, ... in v (-inf beyond E); s_score is the wave's 256-float
+// LDS scratch for group scores.
+__device__ __forceinline__ void topk_token(const TopkParams& p, int64_t t, const float* v, float* s_score) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (t >= p.T) return;
   const int E = p.E;
   const int k = p.rp.k;
   const float NEG = -INFINITY;
-
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = NEG;
-    if (e < E) {
-      float s = 0.f;
-      for (int sp = 0; sp < p.S; ++sp) s += p.part[(sp * p.T + t) * E + e];
-      if (p.bias) s += p.bias[e];
-      v[i] = s;
-      if (p.logits) p.logits[t * E + e] = s;
-    }
-  }
 
   const bool softmax = p.rp.score == MOE_SCORE_SOFTMAX;
   float lmax = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
@@ -109,7 +92,7 @@ __global__ __launch_bounds__(256) void k_topk(TopkParams p) {
     const int G = p.rp.n_groups, per = E / G;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) s_score[wave][lane + 64 * i] = 1.0f / (1.0f + expf(-v[i]));
+      if (lane + 64 * i < E) s_score[lane + 64 * i] = 1.0f / (1.0f + expf(-v[i]));
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     float gs = NEG;
@@ -117,7 +100,7 @@ __global__ __launch_bounds__(256) void k_topk(TopkParams p) {
       float top[4] = {NEG, NEG, NEG, NEG};
       const int n = p.rp.group_topn;
       for (int j = 0; j < per; ++j) {
-        float x = s_score[wave][lane * per + j];
+        float x = s_score[lane * per + j];
         // insert into the descending list top[0..n)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -144,58 +127,85 @@ __global__ __launch_bounds__(256) void k_topk(TopkParams p) {
     }
   }
 
-  int sel_e[kMaxK];
-  float sel_v[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {
-      int be;
-      float bv;
-      if (p.forced) {
-        be = p.forced[t * k + j];
-        bv = NEG;
-        if (be >= 0 && be < E) {
-          const int i = be >> 6, src = be & 63;
-          const float mine = i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
-          bv = __shfl(mine, src, kWave);
-        }
-      } else {
-        bv = NEG;
-        be = 1 << 30;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = lane + 64 * i;
-          if (((cand >> i) & 1u) && better(v[i], e, bv, be)) { bv = v[i]; be = e; }
-        }
-        wave_argmax(bv, be);
-        if ((be & 63) == lane) cand &= ~(1u << (be >> 6));
+  // Slot j is kept by lane j (its expert and logit).  The loops run k times
+  // instead of being unrolled for the largest k: the code runs once per token,
+  // so its size, not its instruction count, is what costs (each new
+  // instruction-cache line is a memory round trip).
+  int my_e = 0;
+  float my_v = NEG;
+#pragma unroll 1
+  for (int j = 0; j < k; ++j) {
+    int be;
+    float bv;
+    if (p.forced) {
+      be = p.forced[t * k + j];
+      bv = NEG;
+      if (be >= 0 && be < E) {
+        const int i = be >> 6, src = be & 63;
+        const float mine = i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+        bv = __shfl(mine, src, kWave);
       }
-      sel_e[j] = be;
-      sel_v[j] = bv;
+    } else {
+      bv = NEG;
+      be = 1 << 30;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        if (((cand >> i) & 1u) && better(v[i], e, bv, be)) { bv = v[i]; be = e; }
+      }
+      wave_argmax(bv, be);
+      if ((be & 63) == lane) cand &= ~(1u << (be >> 6));
+    }
+    if (lane == j) {
+      my_e = be;
+      my_v = bv;
     }
   }
-
+  float my_w = 0.f;
+  if (lane < k && my_e >= 0 && my_e < E)
+    my_w = softmax ? expf(my_v - lmax) / denom : 1.0f / (1.0f + expf(-my_v));
   float wsum = 0.f;
-  float wj[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k) {
-      const bool ok = sel_e[j] >= 0 && sel_e[j] < E;
-      float w = 0.f;
-      if (ok) w = softmax ? expf(sel_v[j] - lmax) / denom : 1.0f / (1.0f + expf(-sel_v[j]));
-      wj[j] = w;
-      wsum += w;
-    }
-  }
+#pragma unroll 1
+  for (int j = 0; j < k; ++j) wsum += __shfl(my_w, j, kWave);     // in slot order
   const bool renorm = p.rp.renormalize != 0 && wsum > 0.f;
+  if (lane < k) {
+    const float w = renorm ? my_w / wsum : my_w;
+    p.ids[t * k + lane] = my_e;
+    p.w[t * k + lane] = w * p.rp.routed_scale;
+  }
+}
+
+// One wave per token, 4 tokens per workgroup: adds the S split-K partials of
+// the router GEMM in a fixed order, adds the bias and selects.
+__global__ __launch_bounds__(256) void k_topk(TopkParams p) {
+  __shared__ float s_score[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (t >= p.T) return;
+  float v[4];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < k && lane == j) {
-      float w = renorm ? wj[j] / wsum : wj[j];
-      p.ids[t * k + j] = sel_e[j];
-      p.w[t * k + j] = w * p.rp.routed_scale;
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = -INFINITY;
+    if (e < p.E) {
+      // the S partials (S <= 16) loaded eight at a time, summed in split order
+      float s = 0.f;
+      for (int s0 = 0; s0 < p.S; s0 += 8) {
+        float pv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          pv[u] = s0 + u < p.S ? p.part[((s0 + u) * p.T + t) * p.E + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < p.S) s += pv[u];
+      }
+      if (p.bias) s += p.bias[e];
+      v[i] = s;
+      if (p.logits) p.logits[t * p.E + e] = s;
     }
   }
+  topk_token(p, t, v, s_score[wave]);
 }
 
 moe_status launch_route(const RouteArgs& a, hipStream_t s) {
