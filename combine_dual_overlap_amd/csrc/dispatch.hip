@@ -418,6 +418,10 @@ __global__ __launch_bounds__(256) void k_disp_gather(const u32x4_t* __restrict__
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave; t < T; t += stride) {
+    // lane j < k holds the position of pair (t, j); a token without a local
+    // pair is skipped before its row is read
+    const int my_pos = lane < k ? inv[t * k + lane] : -1;
+    if (__ballot(my_pos >= 0) == 0) continue;
     const u32x4_t* src = x + t * row_chunks;
     for (int c0 = 0; c0 < row_chunks; c0 += 64 * kChunks) {
       u32x4_t v[kChunks];
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(256) void k_disp_gather(const u32x4_t* __restrict__
         if (c < row_chunks) v[i] = src[c];
       }
       for (int j = 0; j < k; ++j) {
-        const int pos = inv[t * k + j];
+        const int pos = __shfl(my_pos, j, kWave);
         if (pos < 0) continue;
         u32x4_t* dst = x_perm + static_cast<int64_t>(pos) * row_chunks;
 #pragma unroll
@@ -451,6 +455,10 @@ __global__ __launch_bounds__(256) void k_disp_gather_q8(const u32x4_t* __restric
   const int64_t H = static_cast<int64_t>(row_chunks) * 8;
   const int groups = row_chunks / 16;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave; t < T; t += stride) {
+    // as in the bf16 gather: pair positions in lanes j < k, tokens without a
+    // local pair skipped (without inv, k = 1 and row t goes to row t)
+    const int my_pos = lane < k ? (inv ? inv[t * k + lane] : 0) : -1;
+    if (inv && __ballot(my_pos >= 0) == 0) continue;
     const u32x4_t* src = x + t * row_chunks;
     for (int c0 = 0; c0 < row_chunks; c0 += 64 * kChunks) {
       u32x4_t v[kChunks];
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(256) void k_disp_gather_q8(const u32x4_t* __restric
         q[i][1] = fp8x4_rne(f[4] * is, f[5] * is, f[6] * is, f[7] * is);
       }
       for (int j = 0; j < k; ++j) {
-        const int64_t pos = inv ? inv[t * k + j] : t;
+        const int64_t pos = inv ? static_cast<int64_t>(__shfl(my_pos, j, kWave)) : t;
         if (pos < 0) continue;
         uint8_t* dst = xq + pos * H;
 #pragma unroll
