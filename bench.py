@@ -130,11 +130,13 @@ def comm_work(cfg, L, halves, comm_ms, fp8_act=False):
     return out
 
 
-def comm_kernels_alone(cfg, L, half, reps=20):
-    """The data-moving kernels of the comm steps timed alone (HIP events
-    around `reps` back-to-back calls on the current stream), on microbatch 0's
+def comm_kernels_alone(cfg, L, half, reps=20, reps_cold=10):
+    """The data-moving kernels of the comm steps timed alone on microbatch 0's
     routing: the row gather of the dispatch (moe_dispatch_recv; its count and
-    rank kernels excluded) and the combine without the shared-expert slabs."""
+    rank kernels excluded) and the combine without the shared-expert slabs.
+    Warm: HIP events around `reps` back-to-back calls on the current stream
+    (inputs may sit in the 256 MB MALL).  Cold: each call alone between two
+    events, after a read of a 512 MiB scratch buffer has displaced the MALL."""
     import torch
     from combine_dual_overlap_amd import binding as B
     a, b = half
@@ -147,6 +149,7 @@ def comm_kernels_alone(cfg, L, half, reps=20):
     M = int((inv_np >= 0).sum())
     t_hit = int((inv_np >= 0).any(axis=1).sum())
     rows = torch.empty(max(n * cfg.k, 1), cfg.H, dtype=x.dtype, device=x.device)
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device=x.device)     # 512 MiB
     out = torch.empty(n, cfg.H, dtype=x.dtype, device=x.device)
     calls = {"gather": lambda: B.moe_dispatch_recv(x, cfg.k, inv, rows),
              "combine": lambda: B.moe_combine(rows, n, cfg.k, inv, w, out)}
@@ -164,8 +167,20 @@ def comm_kernels_alone(cfg, L, half, reps=20):
         torch.cuda.synchronize()
         avg_s = t0.elapsed_time(t1) / reps / 1e3
         gbs = byts[name] / avg_s / 1e9
+        cold = []
+        for _ in range(reps_cold):
+            scratch.sum()
+            t0.record()
+            calls[name]()
+            t1.record()
+            torch.cuda.synchronize()
+            cold.append(t0.elapsed_time(t1) / 1e3)
+        cold_s = float(np.median(cold))
+        cold_gbs = byts[name] / cold_s / 1e9
         rec.append({"avg_us": round(avg_s * 1e6, 2), "algorithmic_bytes": int(byts[name]),
-                    "achieved_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+                    "achieved_GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                    "cold_median_us": round(cold_s * 1e6, 2), "cold_achieved_GBps": round(cold_gbs, 1),
+                    "cold_frac_of_hbm_peak": round(cold_gbs / HBM_PEAK_GBS, 4)})
     return rec
 
 
