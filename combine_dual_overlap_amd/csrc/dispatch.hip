@@ -22,9 +22,10 @@
 //               block from wave ballots (lanes holding the same expert are
 //               grouped with a ballot loop; rank = popcount of lower lanes) plus
 //               an LDS prefix over the 4 waves; writes perm and inv.
-//  4. gather  - one wave per token: the row is read from HBM once (16-byte
-//               vector loads, several in flight per lane) and written to each of
-//               its k destination rows.  The fp8 variant quantises the row on
+//  4. gather  - one wave per token: the token's k positions are read first
+//               (a token with no local pair is skipped), then the row is read
+//               from HBM once (16-byte vector loads, several in flight per
+//               lane) and written to each of its k destination rows.  The fp8 variant quantises the row on
 //               the way (groups of 128 columns, E8M0 scales; fp8_act.h) and
 //               writes codes and scale bytes instead.
 #include "fp8_act.h"
