@@ -235,7 +235,7 @@ __global__ __launch_bounds__(1024) void k_disp_rank_scan(const int32_t* __restri
   __shared__ int s_wcnt[16][kMidMaxELoc];   // this block's count per wave and expert
   __shared__ int s_wsum[32];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int wave = tid >> 6;
   const int64_t b = blockIdx.x;
   for (int e = tid; e < E_loc; e += 1024) {
     s_pre[e] = 0;
@@ -316,7 +316,6 @@ __global__ __launch_bounds__(1024) void k_disp_rank_scan(const int32_t* __restri
     }
     inv[p] = pos;
   }
-  (void)lane;
 }
 
 // Small batches (few pairs, E_loc <= 256): count, scan and rank in one
