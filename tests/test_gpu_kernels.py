@@ -52,6 +52,38 @@ def test_route_topk(cid):
     assert np.abs(w.cpu().double().numpy()[ok] - ref_w[ok]).max() < 1e-5
 
 
+# Edge shapes of the selection: one expert; k = E; the largest k (16) with 64
+# and 256 experts (one and four experts per lane); experts not a multiple of
+# 64; group-limited routing with k = 16 and with uneven groups; forced ids.
+@pytest.mark.parametrize("E,k,score,renorm,G,TG,forced", [
+    (1, 1, "softmax", False, 1, 1, False), (5, 5, "softmax", True, 1, 1, False),
+    (64, 16, "softmax", False, 1, 1, False), (256, 16, "softmax", True, 1, 1, False),
+    (200, 7, "sigmoid", False, 1, 1, False), (256, 16, "sigmoid", True, 8, 4, False),
+    (96, 3, "sigmoid", True, 4, 2, False), (128, 8, "softmax", True, 1, 1, True)])
+def test_route_edge_shapes(E, k, score, renorm, G, TG, forced):
+    C = _gpu()
+    T, H = 300, 256
+    cfg = W.LayerConfig("edge", T=T, H=H, E=E, k=k, I=64, act="bf16", wdt="bf16", score=score,
+                        renormalize=renorm, n_groups=G, topk_groups=TG)
+    g = torch.Generator().manual_seed(E * 100 + k)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    wr = (torch.randn(E, H, generator=g) * 0.1).to(torch.bfloat16)
+    fids = None
+    if forced:
+        fids = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32)
+    ids, w, logits = _route(C, cfg, x.cuda(), wr.cuda(), forced=None if fids is None else fids.cuda())
+    print(f"route edge E={E} k={k} {score} groups={G}/{TG} forced={forced}", flush=True)
+    ol = O.router_logits(O.decode(W.bits(x), "bf16"), O.decode(W.bits(wr), "bf16"))
+    gl = to_f64(logits)
+    assert (np.abs(gl - ol) <= 1e-4 + 1e-6 * np.abs(ol)).all()
+    fnp = None if fids is None else fids.numpy()
+    ref_ids, ref_w, diff = check_ids(ids.cpu().numpy(), gl, cfg, fnp)
+    ok = ~diff
+    assert np.abs(w.cpu().double().numpy()[ok] - ref_w[ok]).max() < 1e-5
+    if forced:
+        assert np.array_equal(ids.cpu().numpy(), fnp)
+
+
 def test_route_ties_pick_lower_index():
     C = _gpu()
     cfg = W.LayerConfig("ties", T=8, H=128, E=64, k=4, I=64, act="bf16", wdt="bf16")
