@@ -1,6 +1,7 @@
 """Shared helpers of the GPU parity tests: tolerance rule, oracle/GPU glue,
 cached workloads."""
 import functools
+import os
 
 import numpy as np
 import torch
@@ -9,15 +10,24 @@ import oracle as O
 from oracle.routing import route_cfg
 import workloads as W
 
-# Tolerances of the floating-point outputs, relative to the magnitude of what
-# each element sums: |gpu - ref| <= tol * (A + rms(A)/100) with A the oracle's
-# per-element sum of |terms| (for the layer: sum_j |w_j| (|h_j| |W2|^T), plus
-# the shared experts).  The GPU rounds h, y_perm and out to bf16 once each, a
-# first-order error of at most 3 * 2^-9 * A (about 0.6% of A), so the bf16 /
-# fp8-weight tolerances of the layer's statement (1e-2, 5e-2) hold with margin
-# even where the weighted expert outputs cancel; fp32 (tiny config): 1e-4.
-# Without a scale the rule falls back to tol * (|ref| + rms(ref)).
-TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 5e-2}
+# Tolerances of the floating-point outputs.  Two checks, both must hold:
+#  * elementwise, relative to the magnitude of what each element sums:
+#    |gpu - ref| <= tol * (A + rms(A)/100), with A the oracle's per-element sum
+#    of |terms| (for the layer: sum_j |w_j| (|h_j| |W2|^T), plus the shared
+#    experts).  The GPU rounds h, y_perm and out to bf16 once each, and an fp8
+#    weight once more (code value times its block scale, to bf16): a
+#    first-order error of at most 4 * 2^-9 * A (0.8 % of A), so tol = 1e-2
+#    holds for bf16 and fp8 weights alike, even where the weighted expert
+#    outputs cancel;
+#  * over the whole output, relative to the output:
+#    ||gpu - ref||_2 <= tol * ||ref||_2 (the "rel" reading of the layer's
+#    statement).  Independent roundings of relative size <= 2^-9 give a
+#    relative RMS error near 2^-9 / sqrt(3) per rounding, about 0.1 %.
+# The layer's statement allows 1e-2 (bf16) and 5e-2 (fp8 weights); both
+# checks use 1e-2 for fp8 weights too, which the bound above supports.
+# fp32 (tiny config): 1e-4.  Without a scale the elementwise rule falls back
+# to tol * (|ref| + rms(ref)).
+TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 1e-2}
 
 
 def tol_for(cfg) -> float:
@@ -26,11 +36,24 @@ def tol_for(cfg) -> float:
     return TOL["fp8"] if cfg.wdt == "fp8" else TOL["bf16"]
 
 
-def assert_close(gpu, ref, tol, what="", scale=None):
+def _margin_log(line: str):
+    """Appends a parity margin line to $PARITY_LOG (if set)."""
+    path = os.environ.get("PARITY_LOG")
+    if path:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+        with open(path, "a") as f:
+            f.write(f"{test} | {line}\n")
+
+
+def assert_close(gpu, ref, tol, what="", scale=None, rms_tol=None):
+    """Both parity checks (see above).  rms_tol defaults to tol.  Returns the
+    worst elementwise err/A (in units of A) and prints it with the relative
+    RMS error."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     assert np.isfinite(gpu).all(), f"{what}: non-finite values"
+    rms_tol = tol if rms_tol is None else rms_tol
     err = np.abs(gpu - ref)
     if scale is None:
         rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
@@ -40,13 +63,22 @@ def assert_close(gpu, ref, tol, what="", scale=None):
         assert (np.abs(ref) <= scale * (1 + 1e-12) + 1e-300).all(), f"{what}: |ref| exceeds its term magnitude"
         rms = float(np.sqrt(np.mean(scale ** 2))) if scale.size else 0.0
         bound = tol * (scale + rms / 100)
+    ref_norm = float(np.sqrt(np.sum(ref ** 2)))
+    rel_rms = float(np.sqrt(np.sum(err ** 2))) / ref_norm if ref_norm > 0 else float(np.sqrt(np.sum(err ** 2)))
+    worst = float((err / (bound / tol + 1e-300)).max()) if err.size else 0.0
+    line = (f"{what}: max abs err {err.max() if err.size else 0:.3g}, worst err/A {worst:.3g} "
+            f"(tol {tol}), rel RMS {rel_rms:.3g} (tol {rms_tol}), n {err.size}")
     bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err / (bound + 1e-300)), err.shape)
+        _margin_log("FAIL " + line)
         raise AssertionError(f"{what}: {bad.sum()} of {err.size} outside tol {tol}; worst at {i}: "
                              f"gpu {gpu[i]!r} ref {ref[i]!r} bound {bound[i]!r} (max abs err {err.max():.3g})")
-    worst = float((err / (bound / tol + 1e-300)).max()) if err.size else 0.0
-    print(f"  {what}: max abs err {err.max() if err.size else 0:.3g}, worst err/scale {worst:.3g} (tol {tol})")
+    if rel_rms > rms_tol:
+        _margin_log("FAIL " + line)
+        raise AssertionError(f"{what}: relative RMS error {rel_rms:.4g} above {rms_tol}")
+    print("  " + line)
+    _margin_log(line)
     return worst
 
 
@@ -58,6 +90,14 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 def inputs(cid: int, small: bool, seed: int = 0):
     cfg = W.get_config(cid, small=small)
     inp = W.make_inputs(cfg, seed)
+    return inp, W.oracle_view(inp)
+
+
+@functools.lru_cache(maxsize=None)
+def routing_inputs(cid: int, small: bool, seed: int = 0):
+    """The same draws without the expert weights (routing and dispatch only)."""
+    cfg = W.get_config(cid, small=small)
+    inp = W.make_inputs(cfg, seed, weights=False)
     return inp, W.oracle_view(inp)
 
 

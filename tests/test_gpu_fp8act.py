@@ -8,11 +8,15 @@ import torch
 import oracle as O
 import workloads as W
 from conftest import read_golden
-from helpers import assert_close, inputs, to_f64
+from helpers import TOL as _TOL, assert_close, inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 
-TOL = 5e-2
+# fp8 weights and fp8 activations: the codes of x are exact on both sides; h
+# is quantised from fp32 (GPU) and float64 (oracle) sums, so a code may land
+# one step apart where h sits on a rounding boundary (each such flip moves one
+# of I terms by at most 1/8 of its magnitude); y and out are rounded to bf16.
+TOL = _TOL["fp8"]
 
 
 def _B():

@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from helpers import assert_close, check_ids, check_routing, inputs, to_f64, tol_for
+from helpers import assert_close, check_ids, check_routing, inputs, routing_inputs, to_f64, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -139,12 +139,10 @@ def _check_dispatch(cfg, x_cpu, ids_np, g, tile_m=16):
 @pytest.mark.parametrize("small", [True, False])
 def test_dispatch(cid, small):
     C = _gpu()
-    if not small and cid == 4:
-        pytest.skip("the full R1-shaped weights are covered by the layer test")
-    inp, ov = inputs(cid, small)
+    inp, ov = routing_inputs(cid, small)         # dispatch needs x and the ids, not the expert weights
     cfg = inp["cfg"]
     T0 = O.split_point(cfg.T)
-    ids_all = O.moe_layer_expert(ov, tokens=np.arange(1))["ids"]
+    ids_all = O.moe_layer_expert(ov, tokens=np.arange(0))["ids"]
     print(f"dispatch cfg={cfg.name} T={cfg.T}", flush=True)
     for a, b in [(0, T0), (T0, cfg.T)]:
         x = inp["x"][a:b]

@@ -27,6 +27,7 @@ import torch
 
 # tensor ids used in the seed recipe
 TID_X, TID_WR, TID_W13, TID_W2, TID_SH_W13, TID_SH_W2, TID_FORCED, TID_ZIPF = 1, 2, 3, 4, 5, 6, 7, 8
+TID_W13_SPREAD, TID_W2_SPREAD = 9, 10
 
 FP8_BLOCK = 128
 FP8_MAX = 448.0
@@ -58,6 +59,11 @@ class LayerConfig:
     x_std: float = 1.0
     w_std: float = 0.02
     wr_std: float = 0.02
+    # fp8 weights: each 128x128 block of the N(0, w_std) draw is multiplied by
+    # 2^u, u ~ U(-spread, spread), before quantisation, so block scales differ
+    # from block to block (as in trained block-quantised checkpoints) and a
+    # wrong block-scale index shows in the output.  0 = every block alike.
+    fp8_block_spread: float = 0.0
     cfg_id: int = 0
 
     def __post_init__(self):
@@ -97,10 +103,10 @@ CONFIGS = {
     2: LayerConfig("v2lite_decode_bf16", T=256, H=2048, E=64, k=6, I=1408, act="bf16", wdt="bf16",
                    score="softmax", renormalize=False, n_shared=2, shared_I=1408, cfg_id=2),
     3: LayerConfig("qwen3_prefill_fp8w", T=8192, H=2048, E=128, k=8, I=768, act="bf16", wdt="fp8",
-                   score="softmax", renormalize=True, forced_uniform=True, cfg_id=3),
+                   score="softmax", renormalize=True, forced_uniform=True, fp8_block_spread=4.0, cfg_id=3),
     4: LayerConfig("r1_share_fp8w", T=4096, H=7168, E=256, k=8, I=2048, act="bf16", wdt="fp8",
                    score="sigmoid", renormalize=True, n_groups=8, topk_groups=4, group_topn=2,
-                   expert_begin=0, expert_end=32, cfg_id=4),
+                   expert_begin=0, expert_end=32, fp8_block_spread=4.0, cfg_id=4),
     5: LayerConfig("skewed_zipf_bf16", T=6001, H=2048, E=64, k=6, I=1408, act="bf16", wdt="bf16",
                    score="softmax", renormalize=False, zipf_alpha=1.2,
                    seq_lens=[1] * 1000 + [3000] + [1] * 2001, cfg_id=5),
@@ -157,13 +163,25 @@ def quantize_fp8_blocks(w: torch.Tensor):
     return codes[:R, :C].contiguous(), scale.contiguous()
 
 
-def _expert_weights(cfg: LayerConfig, seed: int, tid: int, n_exp: int, rows: int, cols: int):
+def _block_spread(g: torch.Generator, spread: float, rows: int, cols: int) -> torch.Tensor:
+    """[rows, cols] factor 2^u, one u ~ U(-spread, spread) per 128x128 block."""
+    rb, cb = -(-rows // FP8_BLOCK), -(-cols // FP8_BLOCK)
+    u = (torch.rand(rb, cb, generator=g) * 2.0 - 1.0) * spread
+    f = torch.pow(2.0, u)
+    return f.repeat_interleave(FP8_BLOCK, 0).repeat_interleave(FP8_BLOCK, 1)[:rows, :cols]
+
+
+def _expert_weights(cfg: LayerConfig, seed: int, tid: int, n_exp: int, rows: int, cols: int,
+                    spread_tid: int = 0):
     g = _gen(cfg, seed, tid)
     if cfg.wdt == "fp8":
+        gs = _gen(cfg, seed, spread_tid) if cfg.fp8_block_spread > 0 else None
         codes = torch.empty(n_exp, rows, cols, dtype=torch.uint8)
         scales = torch.empty(n_exp, -(-rows // FP8_BLOCK), -(-cols // FP8_BLOCK), dtype=torch.float32)
         for e in range(n_exp):
             w = torch.randn(rows, cols, generator=g) * cfg.w_std
+            if gs is not None:
+                w = w * _block_spread(gs, cfg.fp8_block_spread, rows, cols)
             codes[e], scales[e] = quantize_fp8_blocks(w)
         return codes, scales
     dt = torch.float32 if cfg.wdt == "f32" else torch.bfloat16
@@ -173,8 +191,12 @@ def _expert_weights(cfg: LayerConfig, seed: int, tid: int, n_exp: int, rows: int
     return out, None
 
 
-def make_inputs(cfg: LayerConfig, seed: int = 0) -> dict:
+def make_inputs(cfg: LayerConfig, seed: int = 0, weights: bool = True) -> dict:
     """Draw every input of one layer call as CPU tensors.
+
+    weights=False leaves out the expert weights (w13, w2, their scales and the
+    shared experts: None / empty lists), for checks of routing and dispatch
+    alone; the other tensors are the same draws as with weights.
 
     Keys: x [T,H]; w_router [E,H]; logit_bias [E] f32 or None; forced_ids [T,k]
     int32 or None; w13 [E_loc,2I,H] (gate rows [0,I), up rows [I,2I)); w2
@@ -204,11 +226,13 @@ def make_inputs(cfg: LayerConfig, seed: int = 0) -> dict:
         u = torch.rand(T, E, generator=_gen(cfg, seed, TID_FORCED))
         forced_ids = torch.argsort(u, dim=1)[:, :k].to(torch.int32).contiguous()
 
-    w13, w13_scale = _expert_weights(cfg, seed, TID_W13, cfg.E_loc, 2 * I, H)
-    w2, w2_scale = _expert_weights(cfg, seed, TID_W2, cfg.E_loc, H, I)
+    w13 = w13_scale = w2 = w2_scale = None
+    if weights:
+        w13, w13_scale = _expert_weights(cfg, seed, TID_W13, cfg.E_loc, 2 * I, H, TID_W13_SPREAD)
+        w2, w2_scale = _expert_weights(cfg, seed, TID_W2, cfg.E_loc, H, I, TID_W2_SPREAD)
 
     shared_w13, shared_w2 = [], []
-    if cfg.n_shared > 0:
+    if cfg.n_shared > 0 and weights:
         sh_cfg = cfg.replace(wdt=cfg.act if cfg.wdt == "fp8" else cfg.wdt)
         a, _ = _expert_weights(sh_cfg, seed, TID_SH_W13, cfg.n_shared, 2 * cfg.shared_I, H)
         b, _ = _expert_weights(sh_cfg, seed, TID_SH_W2, cfg.n_shared, H, cfg.shared_I)
