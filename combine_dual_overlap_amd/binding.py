@@ -29,7 +29,7 @@ EXPORTED = [
     "dbo_ctx_last_stats",
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "dbo_moe_layer", "moe_status_string",
     "moe_quant_fp8_rows", "moe_dispatch_fp8", "moe_ffn_fp8_workspace_size", "moe_grouped_ffn_fp8",
-    "moe_dispatch_send", "moe_dispatch_recv",
+    "moe_dispatch_send", "moe_dispatch_recv", "moe_dispatch_noalloc_max_workspace", "moe_dispatch_noalloc",
 ]
 
 
@@ -82,6 +82,9 @@ def lib():
             "moe_dispatch": (_i32, [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
             "moe_get_device_error": (_i32, [_vp, ctypes.POINTER(_i32), _vp]),
+            "moe_dispatch_noalloc_max_workspace": (_sz, []),
+            "moe_dispatch_noalloc": (_i32, [_vp, _i32, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
             "moe_ffn_workspace_size": (_sz, [_i64, _i32, _i32]),
             "moe_ffn_auto_tile": (_i32, [_i32, _i32, _i32, _i32, _i64, _i64, _i32]),
             "moe_grouped_ffn": (_i32, [_vp, _i32, _i32, _i32, _vp, _i32, _i64, _vp, _vp, _i32, _vp, _vp,
@@ -185,6 +188,19 @@ def moe_dispatch(x, topk_ids, E_total, expert_begin, expert_end, counts, offsets
                               tile_m, ptr(counts), ptr(offsets), ptr(tile_offsets), ptr(perm), ptr(inv),
                               ptr(x_perm), ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream)),
            "moe_dispatch")
+
+
+def moe_dispatch_noalloc_max_workspace() -> int:
+    return lib().moe_dispatch_noalloc_max_workspace()
+
+
+def moe_dispatch_noalloc(x, topk_ids, E_total, expert_begin, expert_end, counts, offsets, perm, inv, x_perm,
+                         tile_m=0, tile_offsets=None, stream=None):
+    T, H = x.shape
+    k = topk_ids.shape[1] if topk_ids.dim() == 2 else 1
+    _check(lib().moe_dispatch_noalloc(ptr(x), dtype_code(x), T, H, ptr(topk_ids), k, E_total, expert_begin,
+                                      expert_end, tile_m, ptr(counts), ptr(offsets), ptr(tile_offsets), ptr(perm),
+                                      ptr(inv), ptr(x_perm), stream_handle(stream)), "moe_dispatch_noalloc")
 
 
 def moe_dispatch_send(topk_ids, E_total, expert_begin, expert_end, counts, offsets, perm, inv, ws, tile_m=0,

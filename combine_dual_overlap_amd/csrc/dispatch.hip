@@ -28,6 +28,8 @@
 //               lane) and written to each of its k destination rows.  The fp8 variant quantises the row on
 //               the way (groups of 128 columns, E8M0 scales; fp8_act.h) and
 //               writes codes and scale bytes instead.
+#include <mutex>
+
 #include "fp8_act.h"
 
 namespace dbomoe {
@@ -604,6 +606,67 @@ extern "C" moe_status moe_dispatch(const void* x, moe_dtype act, int64_t T, int3
     return MOE_ERR_MISALIGNED;
   if (T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (ws_bytes < dispatch_ws_bytes(T, k, E_loc)) return MOE_ERR_WORKSPACE;
+  DispatchArgs a{x, act, T, H, topk_ids, k, E_total, expert_begin, expert_end, tile_m,
+                 counts, offsets, tile_offsets, perm, inv, x_perm, ws, 0, nullptr};
+  return launch_dispatch(a, as_stream(stream));
+}
+
+// ---- dispatch without a caller workspace ---------------------------------
+//
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops, harnesses that forbid it): the dispatch workspace
+// (error word, per-block error flags and histograms) lives in this
+// file-scope device array instead.  Each GPU holds its own copy for the life
+// of the process.  Its device address is looked up once per device, with that
+// device current, on the first call there; host code uses only that address.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+constexpr int kNoAllocMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kNoAllocMaxDevices];
+
+static moe_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+extern "C" size_t moe_dispatch_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
+
+extern "C" moe_status moe_dispatch_noalloc(const void* x, moe_dtype act, int64_t T, int32_t H,
+                                           const int32_t* topk_ids, int32_t k, int32_t E_total,
+                                           int32_t expert_begin, int32_t expert_end, int32_t tile_m,
+                                           int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
+                                           int32_t* perm, int32_t* inv, void* x_perm, void* stream) {
+  if (T < 0 || H <= 0 || k < 1 || k > 16 || E_total < 1) return MOE_ERR_INVALID_ARG;
+  if (expert_begin < 0 || expert_end <= expert_begin || expert_end > E_total) return MOE_ERR_INVALID_ARG;
+  const int E_loc = expert_end - expert_begin;
+  if (E_loc > kMaxELoc) return MOE_ERR_UNSUPPORTED;
+  if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (tile_offsets && tile_m <= 0) return MOE_ERR_INVALID_ARG;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !topk_ids || !perm || !inv || !x_perm)) return MOE_ERR_INVALID_ARG;
+  if ((static_cast<int64_t>(H) * dtype_size(act)) % 16) return MOE_ERR_MISALIGNED;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(counts) || !aligned16(offsets) ||
+      (tile_offsets && !aligned16(tile_offsets)) || !aligned16(perm) || !aligned16(inv) || !aligned16(x_perm))
+    return MOE_ERR_MISALIGNED;
+  if (T * k > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (dispatch_ws_bytes(T, k, E_loc) > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const moe_status st = scratch_for_current_device(&ws);
+  if (st != MOE_OK) return st;
+  // Every word of the workspace a call reads is written earlier in the same
+  // call (block histograms and flags by the count kernel, the error word by
+  // the scan), so nothing left by an earlier call needs clearing.
   DispatchArgs a{x, act, T, H, topk_ids, k, E_total, expert_begin, expert_end, tile_m,
                  counts, offsets, tile_offsets, perm, inv, x_perm, ws, 0, nullptr};
   return launch_dispatch(a, as_stream(stream));

@@ -122,6 +122,28 @@ moe_status moe_dispatch(const void* x, moe_dtype act, int64_t T, int32_t H,
                         void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_dispatch_noalloc - moe_dispatch without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * outputs and errors as moe_dispatch, less ws / ws_bytes: the workspace is a
+ * library-owned device array of moe_dispatch_noalloc_max_workspace() bytes
+ * (8 MiB) on each GPU, held until the process ends.  A call whose
+ * moe_dispatch_workspace_size(T, k, E_loc) exceeds that returns
+ * MOE_ERR_WORKSPACE and enqueues nothing.  The call allocates and frees
+ * nothing.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (on different streams, or from several threads without
+ * ordering) race and must not be issued.  Out-of-range ids are skipped as in
+ * moe_dispatch; their device error word stays in the shared array and is not
+ * reported (use moe_dispatch where it is needed).
+ * ------------------------------------------------------------------------- */
+size_t moe_dispatch_noalloc_max_workspace(void);
+moe_status moe_dispatch_noalloc(const void* x, moe_dtype act, int64_t T, int32_t H,
+                                const int32_t* topk_ids, int32_t k, int32_t E_total,
+                                int32_t expert_begin, int32_t expert_end, int32_t tile_m,
+                                int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
+                                int32_t* perm, int32_t* inv, void* x_perm, void* stream);
+
+/* ---------------------------------------------------------------------------
  * fp8 activations: per-row quantisation in groups of 128 columns.
  * The pages name a fused SiLU-mul + fp8 quantisation op that feeds an fp8
  * GEMM ("[Core/DBO][1/N] Add Dual-Batch Overlap mechanism to VLLM", CI
