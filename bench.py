@@ -2,14 +2,23 @@
 
 One step = one dbo_moe_layer call over one batch of synthetic input (routing,
 dispatch, grouped SwiGLU FFN and combine of both microbatches, both streams
-joined).  Default workload: the DeepSeek-V2-Lite-shaped decode layer (T=256
-tokens split 128/128, H=2048, 64 routed experts top-6 + 2 shared experts,
-I=1408, bf16).  Prints one JSON line with the DBO tokens/s (the step captured
-once in a HIP graph and replayed; eager-issued steps beside it), SERIAL and
-UNSPLIT tokens/s, the roofline of the dominant kernel (the gate/up expert
-GEMM), and the CPU oracle timed on a bounded sample.
+joined).  Default workload: the Qwen3-30B-A3B-shaped prefill layer (T=8192
+tokens split 4096/4096, H=2048, 128 experts top-8 with uniform-random expert
+ids, I=768, fp8 e4m3 expert weights with 128x128 block scales, bf16
+activations), the stand-in for the 8192-token prefill benchmark of "[Perf]
+Fix DBO overlap: capture DeepEP event before yield" (Test Plan / Test Result).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+Prints one JSON line: `value` is the DBO step captured once in a HIP graph and
+replayed K times (after W warm-up replays, bracketed by device syncs).  Beside
+it, the schedules DBO, SERIAL, DBO_LATE_EVENT (the event recorded after the
+yield, the over-serialisation the page fixes) and UNSPLIT are timed as
+interleaved repeated trials, graph-replayed and eager, with median and p10/p90
+per schedule and per-round paired ratios; the roofline of the dominant kernel
+(the gate/up expert GEMM) against the per-expert roof; the dispatch and
+combine HBM fractions; the CPU oracle on a bounded sample; and the
+DeepSeek-V2-Lite-shaped decode layer as a secondary record.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
 """
 import argparse
 import hashlib
@@ -86,6 +95,47 @@ def gateup_work(cfg, counts_per_mb, rows_per_mb, fp8_act=False):
             flops += 2.0 * T_mb * cfg.H * 2 * I_sh
         out.append((nbytes, flops))
     return out
+
+
+def ffn_expert_roof(cfg, counts, T_mb, gemm, fp8_act=False, bf16_peak=True):
+    """The per-expert roof of one grouped GEMM launch: the sum over experts
+    with rows of max(flops_e / P_MFMA, bytes_e / B_HBM) (and the shared
+    experts as one dense expert), where bytes_e are the expert's weights (and
+    block scales) read once plus its rows read and its outputs written once.
+    gemm: "gate_up" or "down".  Returns (roof seconds, flops, bytes, seconds
+    of the experts the MFMA bounds, seconds of those HBM bounds)."""
+    w_s = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.wdt]
+    a_s = 4 if cfg.act == "f32" else 2
+    r_s = 1 + 1 / 128 if fp8_act else a_s
+    P = (MFMA_PEAK_TFLOPS["f32" if cfg.act == "f32" else "fp8" if fp8_act else "bf16"]) * 1e12
+    B = HBM_PEAK_GBS * 1e9
+    H, I = cfg.H, cfg.I
+    experts = [(int(n), cfg.wdt, r_s, I) for n in counts if n > 0]
+    I_sh = cfg.n_shared * cfg.shared_I
+    if I_sh:
+        experts.append((T_mb, cfg.act, a_s, I_sh))
+    t_mfma = t_hbm = fl_tot = by_tot = 0.0
+    for n, wdt, rs, Ie in experts:
+        ws = {"f32": 4, "bf16": 2, "fp8": 1}[wdt]
+        if gemm == "gate_up":
+            flops = 4.0 * n * H * Ie
+            nbytes = 2 * Ie * H * ws + n * H * rs + n * Ie * rs
+            if wdt == "fp8":
+                nbytes += (2 * Ie // 128) * (H // 128) * 4
+        else:
+            flops = 2.0 * n * H * Ie
+            out_s = a_s
+            nbytes = H * Ie * ws + n * Ie * rs + n * H * out_s
+            if wdt == "fp8":
+                nbytes += (H // 128) * (Ie // 128) * 4
+        tm, tb = flops / P, nbytes / B
+        if tm >= tb:
+            t_mfma += tm
+        else:
+            t_hbm += tb
+        fl_tot += flops
+        by_tot += nbytes
+    return t_mfma + t_hbm, fl_tot, by_tot, t_mfma, t_hbm
 
 
 def shared_slabs(cfg) -> int:
@@ -184,30 +234,99 @@ def comm_kernels_alone(cfg, L, half, reps=20, reps_cold=10):
     return rec
 
 
-def cpu_baseline(inp, cfg, budget_s: float, fp8_act=False):
-    """The oracle (as it stands) on a bounded sample of the same workload:
-    its first tokens (all of them when one run fits the budget)."""
+def cpu_baseline(inp, cfg, budget_s: float, fp8_act=False, threads: int = 8):
+    """The oracle (as it stands) on a bounded sample of the same workload: its
+    first n tokens, float64 numpy with `threads` BLAS threads (the build
+    host's 8 cores); one warm-up run, then the median of three.  n is the
+    largest of 512, 256, 128, ... tokens whose warm-up run fits a quarter of
+    the budget (a fixed cost, decoding every hit expert's weights, dominates
+    small samples of the fp8-weight layers)."""
     import oracle as O
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    from threadpoolctl import threadpool_limits
     ov = dict(W.oracle_view(inp), fp8_act=fp8_act)
-    n = cfg.T if cfg.T <= 512 else 512
-    sub = O.slice_view(ov, 0, n)
-    t0 = time.perf_counter()
-    O.moe_layer_expert(sub)
-    dt = time.perf_counter() - t0
-    if dt > budget_s and n > 8:
-        n = max(8, int(n * budget_s / dt))
-        sub = O.slice_view(ov, 0, n)
-        t0 = time.perf_counter()
-        O.moe_layer_expert(sub)
-        dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} tokens of the workload, float64 numpy/BLAS moe_layer_expert, one run {dt:.2f} s"}
+    n = min(cfg.T, 512)
+    with threadpool_limits(limits=threads):
+        while True:
+            sub = O.slice_view(ov, 0, n)
+            t0 = time.perf_counter()
+            O.moe_layer_expert(sub)
+            warm = time.perf_counter() - t0
+            if warm <= budget_s / 4 or n <= 16:
+                break
+            n //= 2
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            O.moe_layer_expert(sub)
+            runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} tokens of {cfg.name} (T={cfg.T}), oracle.moe_layer_expert in float64 "
+                      f"numpy/OpenBLAS on {threads} threads; warm-up {warm:.2f} s, then median of 3 runs "
+                      f"{', '.join(f'{r:.2f}' for r in runs)} s"}
+
+
+def _stats(v):
+    v = np.asarray(v, np.float64)
+    return {"median": round(float(np.median(v)), 5), "p10": round(float(np.percentile(v, 10)), 5),
+            "p90": round(float(np.percentile(v, 90)), 5), "n": int(v.size)}
+
+
+def schedule_trials(L, run, schedules, rounds, steps, warmup):
+    """Interleaved repeated trials: each round times `steps` steps of every
+    schedule, graph-replayed and eager, in a rotated order, with HIP events on
+    the current (compute) stream around each trial.  Returns per schedule and
+    mode the ms per step of every round."""
+    import torch
+    graphs = {}
+    for sched in schedules:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run(sched)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(sched)
+        graphs[sched] = g
+    modes = {"graph": lambda sc: graphs[sc].replay(), "eager": lambda sc: run(sc)}
+    for sched in schedules:
+        for m in modes.values():
+            for _ in range(warmup):
+                m(sched)
+    torch.cuda.synchronize()
+    res = {m: {sc: [] for sc in schedules} for m in modes}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for r in range(rounds):
+        order = schedules[r % len(schedules):] + schedules[:r % len(schedules)]
+        for sched in order:
+            for mname, m in modes.items():
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(steps):
+                    m(sched)
+                e1.record()
+                torch.cuda.synchronize()
+                res[mname][sched].append(e0.elapsed_time(e1) / steps)
+    for g in graphs.values():
+        del g
+    return res
+
+
+def summarize_trials(res, T):
+    """Median and p10/p90 of ms per step and tokens/s per schedule, and the
+    per-round paired ratios (time of the other schedule / time of DBO)."""
+    out = {}
+    for mode, per in res.items():
+        o = {"ms_per_step": {sc: _stats(v) for sc, v in per.items()},
+             "tokens_per_s": {sc: _stats([T / (x / 1e3) for x in v]) for sc, v in per.items()}}
+        if "dbo" in per:
+            d = np.asarray(per["dbo"])
+            o["speedup_of_dbo_over"] = {sc: _stats(np.asarray(v) / d) for sc, v in per.items() if sc != "dbo"}
+        out[mode] = o
+    return out
 
 
 def main():
@@ -215,15 +334,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="layer configuration 1..5 (default 2)")
-    ap.add_argument("--schedule", default="dbo", choices=["dbo", "serial", "unsplit", "dbo_late_event", "dbo_recv_hook"])
+    ap.add_argument("--config", type=int, default=3, help="layer configuration 1..5 (default 3)")
+    ap.add_argument("--rounds", type=int, default=9, help="interleaved trial rounds per schedule")
+    ap.add_argument("--trial-steps", type=int, default=20, help="steps per trial")
     ap.add_argument("--comm-cu-budget", type=int, default=0)
     ap.add_argument("--ffn-tile-m", type=int, default=0,
                     help="expert FFN row tile: 0 automatic, 16 weight-streaming kernel, 32/64/128 LDS-tiled kernel")
     ap.add_argument("--fp8-act", action="store_true",
                     help="routed experts with fp8 activations (fp8-weight configurations 3 and 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=24.0)
+    ap.add_argument("--secondary", type=int, default=2,
+                    help="configuration timed as a secondary record after the headline (0: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain elementwise copy of this many MiB three times, the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
@@ -262,52 +384,41 @@ def main():
     def run(sched):
         L.run(sched, comm_cu_budget=args.comm_cu_budget, ffn_tile_m=args.ffn_tile_m)
 
-    def timed(sched):
-        for _ in range(Wm):
-            run(sched)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(K):
-            run(sched)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
+    # The headline: the DBO step captured once in a HIP graph (the whole step,
+    # both streams and their events, one launch), W warm-up replays, then
+    # exactly K timed replays bracketed by device syncs.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run("dbo")
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run("dbo")
+    log(f"bench: warmup {Wm}, timing {K} graph-replayed DBO steps")
+    for _ in range(Wm):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        g.replay()
+    torch.cuda.synchronize()
+    dt_graph = time.perf_counter() - t0
+    del g
 
-    def timed_graph(sched):
-        """The same step captured once in a graph and replayed K times."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            run(sched)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run(sched)
-        for _ in range(Wm):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(K):
-            g.replay()
-        torch.cuda.synchronize()
-        dt_g = time.perf_counter() - t0
-        del g
-        return dt_g
-
-    log(f"bench: warmup {Wm}, timing {K} steps of {args.schedule}, serial and unsplit, eager and graph-replayed")
-    dt = timed(args.schedule)
-    dt_serial = timed("serial")
-    dt_unsplit = timed("unsplit")
-    dt_graph = timed_graph(args.schedule)
-    dt_serial_graph = timed_graph("serial")
+    schedules = ["dbo", "serial", "dbo_late_event", "unsplit"]
+    log(f"bench: {args.rounds} interleaved rounds x {args.trial_steps} steps of {schedules}, graph and eager")
+    trials = summarize_trials(schedule_trials(L, run, schedules, args.rounds, args.trial_steps, 3), T)
 
     # Kernel timing: events around each microbatch's gate/up and down GEMMs on
-    # the compute stream, over K more steps of the same schedule.
-    L.ctx.set_timing(True)
-    for _ in range(min(K, 128)):
-        run(args.schedule)
-    torch.cuda.synchronize()
+    # the compute stream (the stream they are launched on), over more steps of
+    # the DBO schedule.
     n_t = min(K, 128)
+    L.ctx.set_timing(True)
+    for _ in range(n_t):
+        run("dbo")
+    torch.cuda.synchronize()
     times = np.array([L.ctx.ffn_times(b) for b in range(n_t)])     # [n, 4] ms
     L.ctx.set_timing(False)
     gu_ms = times[:, [0, 2]]
@@ -327,22 +438,27 @@ def main():
     T0 = L.ctx.last_stats()["T0"]
     halves = [(0, T0), (T0, T)] if T0 < T else [(0, T)]
     counts = [L.view(mb, "counts", torch.int32, (cfg.E_loc,), T=T).cpu().numpy() for mb in range(len(halves))]
-    work = gateup_work(cfg, counts, [b - a for a, b in halves], args.fp8_act)
+    rows = [b - a for a, b in halves]
+    work = gateup_work(cfg, counts, rows, args.fp8_act)
     bytes_launch = float(np.mean([w[0] for w in work]))
     flops_launch = float(np.mean([w[1] for w in work]))
     avg_s = float(np.mean(gu_ms)) / 1e3
-    ai = flops_launch / bytes_launch
     mfma_peak = MFMA_PEAK_TFLOPS["f32" if cfg.act == "f32" else "fp8" if args.fp8_act else "bf16"]
-    hbm_bound = ai < mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    roofs = {gm: [ffn_expert_roof(cfg, c, n, gm, args.fp8_act) for c, n in zip(counts, rows)]
+             for gm in ("gate_up", "down")}
+    gu_roof = float(np.mean([r[0] for r in roofs["gate_up"]]))
+    dn_roof = float(np.mean([r[0] for r in roofs["down"]]))
+    mfma_part = float(np.mean([r[3] for r in roofs["gate_up"]]))
+    hbm_bound = mfma_part < gu_roof / 2        # the bound that holds most of the per-expert roof
     traffic = read_traffic(f"c{args.config}" + ("_fp8act" if args.fp8_act else ""))
+    ach_gbs = bytes_launch / avg_s / 1e9
+    ach_tf = flops_launch / avg_s / 1e12
     if hbm_bound:
-        achieved = bytes_launch / avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        roof = {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach_gbs / HBM_PEAK_GBS, 4)}
     else:
-        achieved = flops_launch / avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak, "unit": "TFLOP/s",
-                "frac": round(achieved / mfma_peak, 4)}
+        roof = {"bound": "mfma", "achieved": round(ach_tf, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(ach_tf / mfma_peak, 4)}
     roof["traffic"] = traffic
     T_mb0 = halves[0][1] - halves[0][0]
     I_sh = cfg.n_shared * cfg.shared_I
@@ -359,6 +475,12 @@ def main():
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
     roof["algorithmic_bytes_per_launch"] = int(bytes_launch)
     roof["algorithmic_flops_per_launch"] = int(flops_launch)
+    roof["mfma_frac"] = round(ach_tf / mfma_peak, 4)
+    roof["hbm_frac"] = round(ach_gbs / HBM_PEAK_GBS, 4)
+    roof["per_expert_roof_us"] = round(gu_roof * 1e6, 2)
+    roof["frac_of_per_expert_roof"] = round(gu_roof / avg_s, 4)
+    down = {"avg_launch_us": round(float(np.mean(dn_ms)) * 1e3, 2), "per_expert_roof_us": round(dn_roof * 1e6, 2),
+            "frac_of_per_expert_roof": round(dn_roof / (float(np.mean(dn_ms)) / 1e3), 4)}
 
     comm_rec = comm_work(cfg, L, halves, comm, args.fp8_act)
 
@@ -367,11 +489,15 @@ def main():
         log("bench: timing the CPU oracle on a bounded sample")
         base = cpu_baseline(inp, cfg, args.cpu_budget_s, args.fp8_act)
 
-    # The headline is the DBO step replayed from a HIP graph (how a decode
-    # layer is deployed: the whole step, both streams and their events, one
-    # launch); eager numbers sit beside it.
+    secondary = None
+    if args.secondary and args.secondary != args.config:
+        del L
+        torch.cuda.empty_cache()
+        secondary = secondary_record(args.secondary, args, W, DeviceLayer, torch)
+
     value = T * K / dt_graph
     dtype = "fp8" if args.fp8_act else {"f32": "f32", "bf16": "bf16"}[cfg.act]
+    g_tr = trials["graph"]
     rec = {
         "metric": "MoE-layer tokens/sec (DBO vs serial) + MFMA util % and HBM GB/s % of peak",
         "value": round(value, 1),
@@ -388,20 +514,53 @@ def main():
         "config": {"workload": cfg.name, "T": T, "split": [T0, T - T0] if T0 < T else [T], "H": cfg.H,
                    "E": cfg.E, "E_local": cfg.E_loc, "k": cfg.k, "I": cfg.I, "shared_experts": cfg.n_shared,
                    "weights": cfg.wdt, "expert_activations": "fp8" if args.fp8_act else cfg.act,
-                   "schedule": args.schedule, "comm_cu_budget": args.comm_cu_budget,
+                   "schedule": "dbo", "comm_cu_budget": args.comm_cu_budget,
                    "execution": "HIP graph replay of one dbo_moe_layer call per step"},
-        "eager_tokens_per_s": round(T * K / dt, 1),
-        "serial_graph_tokens_per_s": round(T * K / dt_serial_graph, 1),
-        "serial_tokens_per_s": round(T * K / dt_serial, 1),
-        "unsplit_tokens_per_s": round(T * K / dt_unsplit, 1),
-        "dbo_speedup_vs_serial": round(dt_serial_graph / dt_graph, 4),
+        "dbo_speedup_vs_serial": g_tr["speedup_of_dbo_over"]["serial"]["median"],
+        "dbo_speedup_vs_late_event": g_tr["speedup_of_dbo_over"]["dbo_late_event"]["median"],
+        "schedule_trials": {"rounds": args.rounds, "steps_per_trial": args.trial_steps,
+                            "order": "interleaved, rotated each round", **trials},
         "comm_steps": comm_rec,
-        "dbo_speedup_vs_serial_eager": round(dt_serial / dt, 4),
         "kernel_ms": {"gate_up_avg": round(float(np.mean(gu_ms)), 4), "down_avg": round(float(np.mean(dn_ms)), 4)},
+        "down_gemm": down,
         "roofline": roof,
         "cpu_baseline": base,
+        "secondary": secondary,
     }
     print(json.dumps(rec), flush=True)
+
+
+def secondary_record(cid, args, W, DeviceLayer, torch):
+    """A smaller record of another configuration: DBO, SERIAL and
+    DBO_LATE_EVENT in interleaved graph-replayed trials, and the gate/up
+    kernel against its per-expert roof."""
+    cfg = W.get_config(cid)
+    log(f"bench: secondary record {cfg.name}")
+    L = DeviceLayer(W.make_inputs(cfg), device="cuda:0")
+    run = lambda sched: L.run(sched)
+    res = schedule_trials(L, run, ["dbo", "serial", "dbo_late_event"], max(3, args.rounds // 2),
+                          args.trial_steps, 3)
+    res.pop("eager")
+    tr = summarize_trials(res, cfg.T)["graph"]
+    L.ctx.set_timing(True)
+    for _ in range(32):
+        run("dbo")
+    torch.cuda.synchronize()
+    times = np.array([L.ctx.ffn_times(b) for b in range(32)])
+    L.ctx.set_timing(False)
+    gu = times[:, [0, 2]]
+    gu_s = float(np.mean(gu[gu > 0])) / 1e3
+    T0 = L.ctx.last_stats()["T0"]
+    halves = [(0, T0), (T0, cfg.T)]
+    counts = [L.view(mb, "counts", torch.int32, (cfg.E_loc,), T=cfg.T).cpu().numpy() for mb in range(2)]
+    work = gateup_work(cfg, counts, [b - a for a, b in halves])
+    nbytes = float(np.mean([w[0] for w in work]))
+    roof = float(np.mean([ffn_expert_roof(cfg, c, b - a, "gate_up")[0] for c, (a, b) in zip(counts, halves)]))
+    return {"workload": cfg.name, "T": cfg.T, "tokens_per_s_graph": tr["tokens_per_s"],
+            "speedup_of_dbo_over": tr["speedup_of_dbo_over"],
+            "gate_up": {"avg_launch_us": round(gu_s * 1e6, 2), "hbm_GBps": round(nbytes / gu_s / 1e9, 1),
+                        "hbm_frac": round(nbytes / gu_s / 1e9 / HBM_PEAK_GBS, 4),
+                        "frac_of_per_expert_roof": round(roof / gu_s, 4)}}
 
 
 if __name__ == "__main__":

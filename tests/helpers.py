@@ -27,13 +27,27 @@ import workloads as W
 # checks use 1e-2 for fp8 weights too, which the bound above supports.
 # fp32 (tiny config): 1e-4.  Without a scale the elementwise rule falls back
 # to tol * (|ref| + rms(ref)).
-TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 1e-2}
+# fp8 activations: h is itself quantised to fp8, a decision that fp32 (GPU)
+# and float64 (oracle) sums can take one code apart where h sits on a
+# rounding boundary; one such flip moves one term by an fp8 step (1/16 to
+# 1/8 of it), which is a few % of A where that term dominates (measured up to
+# 2.7 % of A on the Qwen3-shaped layer).  The elementwise check then takes
+# the statement's fp8 figure, 5e-2, while the output-relative check stays at
+# 1e-2; the FFN test also checks the h codes themselves against the oracle.
+TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 1e-2, "fp8_act": 5e-2}
+RMS_TOL_FP8_ACT = 1e-2
 
 
-def tol_for(cfg) -> float:
+def tol_for(cfg, fp8_act: bool = False) -> float:
     if cfg.act == "f32":
         return TOL["f32"]
+    if fp8_act:
+        return TOL["fp8_act"]
     return TOL["fp8"] if cfg.wdt == "fp8" else TOL["bf16"]
+
+
+def rms_tol_for(cfg, fp8_act: bool = False) -> float:
+    return RMS_TOL_FP8_ACT if fp8_act else tol_for(cfg)
 
 
 def _margin_log(line: str):

@@ -43,3 +43,29 @@ def test_shared_slabs_match_the_chunk_rule():
     # down projection (K = 2816) is cut into two chunks of 1408
     assert bench.shared_slabs(W.get_config(2)) == 2
     assert bench.shared_slabs(W.get_config(3)) == 0
+
+
+def test_per_expert_roof_by_hand():
+    """Sum over experts of max(flops / 2.5 PFLOP/s, bytes / 8 TB/s): with 256
+    rows each, the Qwen3-shaped gate/up experts are MFMA-bound (644 ns of
+    flops against 574 ns of bytes each); the down experts HBM-bound."""
+    cfg = W.get_config(3)
+    counts = np.full(128, 256)
+    counts[0] = 0
+    t, fl, by, t_mfma, t_hbm = bench.ffn_expert_roof(cfg, counts, 4096, "gate_up")
+    f_e = 4 * 256 * 2048 * 768
+    b_e = 2 * 768 * 2048 + 256 * 2048 * 2 + 256 * 768 * 2 + 12 * 16 * 4
+    assert f_e / 2.5e15 > b_e / 8e12
+    assert abs(t - 127 * f_e / 2.5e15) < 1e-12 and t_hbm == 0.0
+    assert fl == 127 * f_e and by == 127 * b_e
+    t, fl, by, t_mfma, t_hbm = bench.ffn_expert_roof(cfg, counts, 4096, "down")
+    f_e = 2 * 256 * 2048 * 768
+    b_e = 2048 * 768 + 256 * 768 * 2 + 256 * 2048 * 2 + 16 * 6 * 4
+    assert b_e / 8e12 > f_e / 2.5e15
+    assert abs(t - 127 * b_e / 8e12) < 1e-12 and t_mfma == 0.0
+    # decode: the shared experts count as one dense expert over the microbatch
+    cfg2 = W.get_config(2)
+    t2, _, by2, _, _ = bench.ffn_expert_roof(cfg2, np.full(64, 12), 128, "gate_up")
+    shared = 2 * 2816 * 2048 * 2 + 128 * 2048 * 2 + 128 * 2816 * 2
+    routed = 64 * (2 * 1408 * 2048 * 2 + 12 * 2048 * 2 + 12 * 1408 * 2)
+    assert by2 == routed + shared and abs(t2 - (routed + shared) / 8e12) < 1e-12

@@ -8,7 +8,7 @@ import torch
 import oracle as O
 import workloads as W
 from conftest import read_golden
-from helpers import TOL as _TOL, assert_close, inputs, to_f64
+from helpers import RMS_TOL_FP8_ACT, TOL as _TOL, assert_close, inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -16,7 +16,10 @@ pytestmark = pytest.mark.gpu
 # is quantised from fp32 (GPU) and float64 (oracle) sums, so a code may land
 # one step apart where h sits on a rounding boundary (each such flip moves one
 # of I terms by at most 1/8 of its magnitude); y and out are rounded to bf16.
-TOL = _TOL["fp8"]
+# Elementwise 5e-2 of A, output-relative 1e-2 (helpers).  The FFN test
+# checks the h codes themselves and y from the GPU's own h at 1e-2.
+TOL = _TOL["fp8_act"]
+RTOL = RMS_TOL_FP8_ACT
 
 
 def _B():
@@ -150,13 +153,75 @@ def test_dispatch_send_recv_fp8_equals_one_call():
         assert torch.equal(a, b)
 
 
-def _ffn_fp8(B, xq, xs, I, offsets, E_loc, w13, w2, s13, s2, tile_m=0):
+def _ffn_fp8(B, xq, xs, I, offsets, E_loc, w13, w2, s13, s2, tile_m=0, with_h=False):
     cap, H = xq.shape
     y = torch.full((cap, H), float("nan"), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(max(B.moe_ffn_fp8_workspace_size(cap, I), 256), dtype=torch.uint8, device="cuda")
     B.moe_grouped_ffn_fp8(xq, xs, I, offsets, E_loc, w13, w2, s13, s2, y, ws, tile_m=tile_m)
     torch.cuda.synchronize()
-    return y
+    if not with_h:
+        return y
+    # the workspace holds h: codes [cap, I], then (256-byte aligned) E8M0 bytes [cap, I/128]
+    w = ws.cpu().numpy()
+    hq = w[:cap * I].reshape(cap, I)
+    off = -(-cap * I // 256) * 256
+    hs = w[off:off + cap * (I // 128)].reshape(cap, I // 128)
+    return y, hq, hs
+
+
+_POS = O.FP8_E4M3FN_TABLE[:0x7F]          # magnitudes of codes 0x00..0x7E, increasing
+
+
+def _check_h_decisions(hq, hs, h64, dh, what):
+    """The GPU's h codes and scale bytes against the oracle's float64 h, given
+    dh, a bound on |h_gpu - h| from the fp32 arithmetic: the group exponent
+    may differ only where the group's amax lies within the group's largest dh
+    of a bound 448 * 2^e; a code may differ from the oracle's rounding of h
+    only if it is a correct rounding of some value within dh of h, i.e. its
+    value lies within dh plus half a code step of h (scaled by 2^-e).
+    Returns the number of codes that differ."""
+    n, I = h64.shape
+    codes, e = O.quant_rows_fp8(h64)
+    e_gpu = hs.astype(np.int64) - 127
+    amax = np.abs(h64.reshape(n, I // 128, 128)).max(axis=2)
+    dmax = dh.reshape(n, I // 128, 128).max(axis=2)
+    near_bound = (np.abs(amax - 448.0 * np.ldexp(1.0, e)) <= dmax) | \
+                 (np.abs(amax - 448.0 * np.ldexp(1.0, e - 1)) <= dmax)
+    bad_e = (e_gpu != e) & ~near_bound
+    assert not bad_e.any(), f"{what}: {bad_e.sum()} h group exponents differ away from a bound"
+    same_e = np.repeat(e_gpu == e, 128, axis=1)
+    inv = np.ldexp(1.0, -np.repeat(e, 128, axis=1))
+    a = h64 * inv                                            # the oracle's h in code units
+    mag = (hq & 0x7F).astype(np.int64)
+    v = np.where(hq & 0x80, -1.0, 1.0) * _POS[np.minimum(mag, 0x7E)]
+    half = 0.5 * np.maximum(_POS[np.minimum(mag + 1, 0x7E)] - _POS[np.minimum(mag, 0x7E)],
+                            _POS[np.minimum(mag, 0x7E)] - _POS[np.maximum(mag - 1, 0)])
+    diff = (hq != codes) & same_e
+    ok = ~diff | ((mag <= 0x7E) & (np.abs(v - a) <= dh * inv + half))
+    if not ok.all():
+        r, c = np.nonzero(~ok)
+        det = "; ".join(f"({r[i]},{c[i]}) gpu {hq[r[i], c[i]]:#04x} oracle {codes[r[i], c[i]]:#04x} "
+                        f"h {h64[r[i], c[i]]:.9g} scaled {a[r[i], c[i]]:.9g} "
+                        f"dh {dh[r[i], c[i]] * inv[r[i], c[i]]:.3g} e {e[r[i], c[i] // 128]}"
+                        for i in range(min(6, r.size)))
+        raise AssertionError(f"{what}: {int((~ok).sum())} h codes are no rounding of h within its error "
+                             f"bound: {det}")
+    return int(diff.sum())
+
+
+def _h_and_bound(xq, w13, I):
+    """float64 h = silu(g) * u of the fp8 expert and a bound on the error of
+    the same h computed in fp32: |dg| <= K 2^-23 sum_k |x_k w_k| (a dot
+    product's rounding bound, doubled for the block-scale products), same for
+    u, then dh = |silu'(g) u| dg + |silu(g)| du + 4 ulp of h."""
+    K = xq.shape[1]
+    g, u = xq @ w13[:I].T, xq @ w13[I:].T
+    dg = K * 2.0 ** -23 * (np.abs(xq) @ np.abs(w13[:I]).T)
+    du = K * 2.0 ** -23 * (np.abs(xq) @ np.abs(w13[I:]).T)
+    sg = 1.0 / (1.0 + np.exp(-g))
+    h = g * sg * u
+    dh = np.abs(sg * (1.0 + g * (1.0 - sg)) * u) * dg + np.abs(g * sg) * du + 4 * 2.0 ** -24 * np.abs(h)
+    return h, dh
 
 
 @pytest.mark.parametrize("cid", [3, 4])
@@ -172,13 +237,32 @@ def test_grouped_ffn_fp8_matches_oracle(cid, tile_m):
     xq = torch.empty(M, cfg.H, dtype=torch.uint8, device="cuda")
     xs = torch.empty(M, cfg.H // 128, dtype=torch.uint8, device="cuda")
     B.moe_quant_fp8_rows(x_perm.cuda(), xq, xs)
-    y = _ffn_fp8(B, xq, xs, cfg.I, torch.from_numpy(ref["offsets"]).cuda(), cfg.E_loc, inp["w13"].cuda(),
-                 inp["w2"].cuda(), inp["w13_scale"].cuda(), inp["w2_scale"].cuda(), tile_m)
+    y, hq, hs = _ffn_fp8(B, xq, xs, cfg.I, torch.from_numpy(ref["offsets"]).cuda(), cfg.E_loc,
+                         inp["w13"].cuda(), inp["w2"].cuda(), inp["w13_scale"].cuda(), inp["w2_scale"].cuda(),
+                         tile_m, with_h=True)
     xp64 = O.decode(W.bits(x_perm), "bf16")
+    print(f"ffn fp8 cfg={cfg.name} M={M} tile_m={tile_m}", flush=True)
     want, scale = O.grouped_ffn_fp8act_ref(xp64, ref["offsets"], lambda e: O.expert_weights(ov, e),
                                            with_scale=True)
-    print(f"ffn fp8 cfg={cfg.name} M={M} tile_m={tile_m}", flush=True)
-    assert_close(to_f64(y), want, TOL, f"y_perm fp8-act {cfg.name}", scale)
+    assert_close(to_f64(y), want, TOL, f"y_perm fp8-act {cfg.name}", scale, rms_tol=RTOL)
+    # the h decisions, then y from the GPU's own h at the bf16 tolerance
+    xq64 = O.fp8_roundtrip_rows(xp64)
+    h64 = np.zeros((M, cfg.I))
+    dh = np.zeros((M, cfg.I))
+    y_h = np.zeros((M, cfg.H))
+    s_h = np.zeros((M, cfg.H))
+    hg = O.dequant_rows_fp8(hq[:M], hs[:M].astype(np.int64) - 127)
+    offs = ref["offsets"]
+    for e in range(cfg.E_loc):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if b > a:
+            w13, w2 = O.expert_weights(ov, e)
+            h64[a:b], dh[a:b] = _h_and_bound(xq64[a:b], w13, cfg.I)
+            y_h[a:b] = hg[a:b] @ w2.T
+            s_h[a:b] = np.abs(hg[a:b]) @ np.abs(w2).T
+    flips = _check_h_decisions(hq[:M], hs[:M], h64, dh, f"h fp8-act {cfg.name}")
+    print(f"  h codes: {flips} of {hq[:M].size} differ from the oracle's, each within the fp32 error bound")
+    assert_close(to_f64(y), y_h, _TOL["fp8"], f"y_perm from the GPU's h {cfg.name}", s_h)
 
 
 def test_grouped_ffn_fp8_ragged_experts():
@@ -203,7 +287,7 @@ def test_grouped_ffn_fp8_ragged_experts():
     for tm in (64, 128):
         y = _ffn_fp8(B, xq, xs, I, torch.from_numpy(offsets).cuda(), E, w13c.cuda(), w2c.cuda(), s13.cuda(),
                      s2.cuda(), tm)
-        assert_close(to_f64(y), want, TOL, f"ragged fp8-act tile_m={tm}", scale)
+        assert_close(to_f64(y), want, TOL, f"ragged fp8-act tile_m={tm}", scale, rms_tol=RTOL)
 
 
 def test_grouped_ffn_fp8_long_k_register_ring_kernel():
@@ -229,7 +313,7 @@ def test_grouped_ffn_fp8_long_k_register_ring_kernel():
     for tm in (64, 128):
         y = _ffn_fp8(B, xq, xs, I, torch.from_numpy(offsets).cuda(), E, w13c.cuda(), w2c.cuda(), s13.cuda(),
                      s2.cuda(), tm)
-        assert_close(to_f64(y), want, TOL, f"long K fp8-act tile_m={tm}", scale)
+        assert_close(to_f64(y), want, TOL, f"long K fp8-act tile_m={tm}", scale, rms_tol=RTOL)
 
 
 def test_grouped_ffn_fp8_rejects_bad_shapes():
@@ -274,7 +358,7 @@ def test_layer_fp8act_small(cid, schedule):
     T0 = (cfg.T + 1) // 2
     ids = _gpu_ids(L, cfg, T0)
     ref = O.moe_layer_expert(dict(ov, fp8_act=True, forced_ids=ids.astype(np.int32)))
-    assert_close(to_f64(out), ref["out"], TOL, f"out fp8-act {cfg.name} {schedule}", ref["scale"])
+    assert_close(to_f64(out), ref["out"], TOL, f"out fp8-act {cfg.name} {schedule}", ref["scale"], rms_tol=RTOL)
 
 
 @pytest.mark.parametrize("cid", [3, 4])
@@ -302,4 +386,4 @@ def test_layer_fp8act_full_size_sampled(cid):
     sample = np.unique(np.concatenate([[0, T0 - 1, T0, cfg.T - 1], rng.integers(0, cfg.T, 12)]))
     ref = O.moe_layer_expert(dict(ov, fp8_act=True, forced_ids=ids.astype(np.int32)), tokens=sample)
     assert_close(to_f64(out[torch.from_numpy(sample).cuda()]), ref["out"], TOL, f"out fp8-act {cfg.name}",
-                 ref["scale"])
+                 ref["scale"], rms_tol=RTOL)

@@ -102,3 +102,28 @@ def test_fp8_block_scales_differ_across_blocks():
         for s in (inp["w13_scale"], inp["w2_scale"]):
             r = (s.amax(dim=(1, 2)) / s.amin(dim=(1, 2))).log2()
             assert float(r.min()) > 3.0, (cid, r)
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_rule_with_fp8_activations_rejects_planted_mistakes(cid):
+    """fp8 activations: elementwise 5e-2 of A, output-relative 1e-2.  The
+    correct output rounded to bf16 passes; a 10 % error and the block-scale
+    indexing mistakes fail."""
+    from helpers import rms_tol_for
+    cfg = W.get_config(cid, small=True)
+    ov = dict(W.oracle_view(W.make_inputs(cfg)), fp8_act=True)
+    ref = O.moe_layer_expert(ov)
+    tol, rtol = tol_for(cfg, fp8_act=True), rms_tol_for(cfg, fp8_act=True)
+    assert_close(_bf16(ref["out"]), ref["out"], tol, f"{cfg.name} fp8-act, out rounded", ref["scale"], rms_tol=rtol)
+    s13, s2 = ov["w13_scale"], ov["w2_scale"]
+    mutants = {
+        "x1.10": ref["out"] * 1.10,
+        "scale K block + 1": O.moe_layer_expert(dict(ov, w13_scale=np.roll(s13, -1, axis=2),
+                                                     w2_scale=np.roll(s2, -1, axis=2)))["out"],
+        "first K block scale only": O.moe_layer_expert(dict(
+            ov, w13_scale=np.ascontiguousarray(np.broadcast_to(s13[:, :, :1], s13.shape)),
+            w2_scale=np.ascontiguousarray(np.broadcast_to(s2[:, :, :1], s2.shape))))["out"],
+    }
+    for name, got in mutants.items():
+        with pytest.raises(AssertionError):
+            assert_close(got, ref["out"], tol, f"{cfg.name} fp8-act planted: {name}", ref["scale"], rms_tol=rtol)
