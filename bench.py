@@ -329,6 +329,87 @@ def summarize_trials(res, T):
     return out
 
 
+COMM_KERNELS = ("k_disp_", "k_combine")
+
+
+def overlap_from_trace(db_path: str, gap_us: float = 300.0):
+    """Per-step overlap of a rocprofv3 kernel trace (rocpd SQLite database)
+    of `bench.py --trace-steps`: the library's kernels are cut into steps at
+    idle gaps longer than gap_us (the trace mode synchronises and pauses
+    between steps) and into schedules at the longer pauses between them.  Per
+    step: the wall time from the first kernel start to the last kernel end,
+    the union of comm-kernel intervals (dispatch and combine), the union of
+    compute-kernel intervals (router, top-k, expert GEMMs), and their
+    intersection.  overlap % = intersection / step time; hidden comm % =
+    intersection / comm union; exposed comm = step time - compute union."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    rows = [(n, s, e) for n, s, e in con.execute("select name, start, end from kernels order by start")
+            if "dbomoe::" in n]
+    if not rows:
+        raise SystemExit(f"no library kernels in {db_path}")
+
+    def union(iv):
+        iv = sorted(iv)
+        out = []
+        for a, b in iv:
+            if out and a <= out[-1][1]:
+                out[-1][1] = max(out[-1][1], b)
+            else:
+                out.append([a, b])
+        return out
+
+    def length(u):
+        return sum(b - a for a, b in u)
+
+    def inter(u, v):
+        i = j = 0
+        tot = 0
+        while i < len(u) and j < len(v):
+            a, b = max(u[i][0], v[j][0]), min(u[i][1], v[j][1])
+            if b > a:
+                tot += b - a
+            if u[i][1] < v[j][1]:
+                i += 1
+            else:
+                j += 1
+        return tot
+
+    steps, cur, last_end = [], [], None
+    for n, s0, e0 in rows:
+        if last_end is not None and s0 - last_end > gap_us * 1e3:
+            steps.append(cur)
+            cur = []
+        cur.append((n, s0, e0))
+        last_end = e0 if last_end is None else max(last_end, e0)
+    steps.append(cur)
+    recs = []
+    for st in steps:
+        comm = union([[s0, e0] for n, s0, e0 in st if any(k in n for k in COMM_KERNELS)])
+        comp = union([[s0, e0] for n, s0, e0 in st if not any(k in n for k in COMM_KERNELS)])
+        wall = max(e0 for _, _, e0 in st) - min(s0 for _, s0, _ in st)
+        recs.append({"start": min(s0 for _, s0, _ in st), "kernels": len(st), "wall_us": wall / 1e3,
+                     "comm_us": length(comm) / 1e3, "compute_us": length(comp) / 1e3,
+                     "overlap_us": inter(comm, comp) / 1e3})
+    return recs
+
+
+def trace_steps(L, run, schedules, n, torch):
+    """Trace mode: n steps of every schedule, each step alone (synchronised,
+    then a 1 ms pause), 5 ms between schedules, for a kernel trace."""
+    for sched in schedules:
+        for _ in range(3):
+            run(sched)
+        torch.cuda.synchronize()
+        time.sleep(0.005)
+        for _ in range(n):
+            run(sched)
+            torch.cuda.synchronize()
+            time.sleep(0.001)
+        time.sleep(0.005)
+        log(f"bench: traced {n} separated steps of {sched}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,11 +427,20 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=24.0)
     ap.add_argument("--secondary", type=int, default=2,
                     help="configuration timed as a secondary record after the headline (0: none)")
+    ap.add_argument("--trace-steps", type=int, default=0,
+                    help="trace mode: run this many separated steps of DBO, SERIAL and DBO_LATE_EVENT (eager) "
+                         "for a rocprofv3 kernel trace, then exit")
+    ap.add_argument("--overlap-from", default=None,
+                    help="print the per-step overlap summary of a rocprofv3 kernel-trace database written "
+                         "in trace mode (no GPU needed), then exit")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain elementwise copy of this many MiB three times, the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
     args = ap.parse_args()
 
+    if args.overlap_from:
+        print_overlap(args.overlap_from, ["dbo", "serial", "dbo_late_event"])
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the layer is one GPU's share of the expert-parallel work "
               f"and no multi-GPU path is built (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -383,6 +473,10 @@ def main():
 
     def run(sched):
         L.run(sched, comm_cu_budget=args.comm_cu_budget, ffn_tile_m=args.ffn_tile_m)
+
+    if args.trace_steps:
+        trace_steps(L, run, ["dbo", "serial", "dbo_late_event"], args.trace_steps, torch)
+        return
 
     # The headline: the DBO step captured once in a HIP graph (the whole step,
     # both streams and their events, one launch), W warm-up replays, then
@@ -528,6 +622,29 @@ def main():
         "secondary": secondary,
     }
     print(json.dumps(rec), flush=True)
+
+
+def print_overlap(db_path: str, schedules):
+    """Markdown summary of overlap_from_trace: steps are grouped by schedule
+    in the order trace mode runs them (each schedule's separated steps)."""
+    recs = overlap_from_trace(db_path)
+    # schedules are separated by the 5 ms pauses: cut where the gap to the previous step exceeds 3 ms
+    groups, cur = [], [recs[0]]
+    for a, b in zip(recs, recs[1:]):
+        if b["start"] - (a["start"] + a["wall_us"] * 1e3) > 3e6:
+            groups.append(cur)
+            cur = []
+        cur.append(b)
+    groups.append(cur)
+    groups = [g for g in groups if len(g) > 3]        # drop the warm-up clusters
+    print("| schedule | steps | step us (median) | compute us | comm us | overlap us | overlap % of step | "
+          "comm hidden % | exposed comm us |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for name, g in zip(schedules, groups[-len(schedules):]):
+        med = lambda key: float(np.median([r[key] for r in g]))
+        wall, comp, comm, ov = med("wall_us"), med("compute_us"), med("comm_us"), med("overlap_us")
+        print(f"| {name} | {len(g)} | {wall:.1f} | {comp:.1f} | {comm:.1f} | {ov:.1f} | {100 * ov / wall:.1f} | "
+              f"{100 * ov / comm:.1f} | {wall - comp:.1f} |")
 
 
 def secondary_record(cid, args, W, DeviceLayer, torch):
