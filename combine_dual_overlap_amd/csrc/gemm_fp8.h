@@ -377,10 +377,6 @@ __global__ __launch_bounds__(kF8Threads, 2) void k_gemm_f8(F8Params p) {
 // LDS read (it cannot tell the three stage buffers apart); the kernel counts
 // them itself with s_waitcnt.  The assembly sets M0, which the compiler does
 // not use anywhere in these kernels (checked in the generated code).
-__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gptr) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(gptr) : "memory");
-}
 
 // ---------------------------------------------------------------------------
 // The same GEMM with the staging through LDS DMA: three LDS stages of BM + 256

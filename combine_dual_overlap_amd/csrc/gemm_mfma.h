@@ -32,6 +32,8 @@
 //    in one scale block, and so do the 64 gate or 64 up rows of a tile).
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace dbomoe {
@@ -227,6 +229,72 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(const u32x4_t& q, float s, u32
   }
   lo = u32x4_t{out[0], out[1], out[2], out[3]};
   hi = u32x4_t{out[4], out[5], out[6], out[7]};
+}
+
+// Epilogue of a tile: gate/up applies SiLU(gate) * up and rounds h to bf16;
+// down rounds y to bf16; the router writes fp32 logits (+ bias).
+template <int BM, int WAVES_M, int WAVES_N, int MODE, int BN>
+__device__ __forceinline__ void store_tile(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
+                                           const f32x4_t (&acc)[TileShape<BM, WAVES_M, WAVES_N, BN>::TM]
+                                                                [TileShape<BM, WAVES_M, WAVES_N, BN>::TN]) {
+  using S = TileShape<BM, WAVES_M, WAVES_N, BN>;
+  constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int nt = t.nt;
+  // Epilogue.  Accumulator element r of lane l in a 16x16 tile is
+  // (row 4*(l/16) + r, column l%16).
+  const int col_in = lane & 15;
+  const int row_q = (lane >> 4) * 4;
+  if constexpr (MODE == MODE_GATEUP) {
+    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN / 2; ++tn) {
+        const int col = nt * (BN / 2) + wn * (WN / 2) + tn * 16 + col_in;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
+          if (mr < t.rows) {
+            const float gt = acc[tm][tn][r];
+            const float u = acc[tm][tn + TN / 2][r];
+            C[(t.row_begin + mr) * g.ldc + col] = f32_to_bf16(silu_f32(gt) * u);
+          }
+        }
+      }
+  } else if constexpr (MODE == MODE_DOWN) {
+    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int col = nt * BN + wn * WN + tn * 16 + col_in;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
+          if (mr < t.rows) C[(t.row_begin + mr) * g.ldc + col] = f32_to_bf16(acc[tm][tn][r]);
+        }
+      }
+  } else {
+    float* C = static_cast<float*>(g.C) + blockIdx.y * p.split_c;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int col = nt * BN + wn * WN + tn * 16 + col_in;
+        if (col < g.N) {
+          const float b = p.bias ? p.bias[col] : 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
+            if (mr < t.rows) C[(t.row_begin + mr) * g.ldc + col] = acc[tm][tn][r] + b;
+          }
+        }
+      }
+  }
 }
 
 template <int BM, int WAVES_M, int WAVES_N, int MODE, bool FP8, int BN, int BK>
@@ -480,57 +548,211 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
     compute_stage(0);
   }
 
-  // Epilogue.  Accumulator element r of lane l in a 16x16 tile is
-  // (row 4*(l/16) + r, column l%16).
-  const int col_in = lane & 15;
-  const int row_q = (lane >> 4) * 4;
-  if constexpr (MODE == MODE_GATEUP) {
-    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
+  store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc);
+}
+
+// One LDS DMA (global_load_lds_dwordx4): each lane's 16 bytes land at
+// lds_addr + 16 * lane, so one wave instruction fills 1 KB of LDS.  Written as
+// inline assembly with its completion counted by hand (s_waitcnt vmcnt): the
+// compiler's own accounting would wait for every DMA in flight before any
+// LDS read.  No register is written, so nothing the compiler owns is in flight.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gptr) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(gptr) : "memory");
+}
+
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);      // vmcnt(N); expcnt and lgkmcnt not waited for
+}
+
+// The 128 x 128 tile of gemm_tile with its activation rows staged by LDS DMA
+// (and bf16 weight rows too): no register ring and no LDS stores for them.
+// A synthetic stage probe on MI355X (128 x 128 tile, 64-wide K stages, two
+// workgroups per CU, L2-resident data) ran 1.05-1.16 PFLOP/s with register
+// staging and LDS stores and 1.41-1.52 PFLOP/s with DMA staging.  fp8 weights
+// still take the register path: each code is expanded once, value(code)
+// times its block scale rounded to bf16, and stored to LDS (the same
+// arithmetic as gemm_tile, so the outputs are bitwise equal).
+// Each 8-row group of a stage is one DMA: lane l carries row l / 8 of the
+// group and that row's 16-byte chunk (l % 8) ^ (l / 8), so the chunks land in
+// the XOR-swizzled order the fragment reads expect.
+// Schedule per stage kt (LDS buffer kt % 2): issue the DMA of stage kt + 1
+// into the other buffer and the fp8 weight loads of stage kt + 2 into the
+// register slot just freed; MFMAs of stage kt; expand and store the fp8
+// weights of stage kt + 1; wait for this wave's DMA of stage kt + 1 (vmcnt:
+// at most the newer weight loads may still be in flight); barrier.
+template <int MODE, bool FP8>
+__device__ __forceinline__ void gemm_tile_dma(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
+                                              bf16_t (*sA)[128 * kBK], bf16_t (*sB)[128 * kBK]) {
+  constexpr int BM = 128, BN = kBN, BK = kBK, WAVES_M = 2, WAVES_N = 2;
+  using S = TileShape<BM, WAVES_M, WAVES_N, BN>;
+  constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
+  constexpr int NQ = BM / 8 / 4;                  // 8-row DMA groups per wave per stage
+  constexpr int CB = BN * (BK / 16) / 256;        // fp8: 16-byte weight chunks per thread per stage
+  constexpr int STAGE_BYTES = BM * BK * 2;
+  static_assert(BN == BM, "A and B DMA groups share the row mapping");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int K = g.K, KT = K / BK, nt = t.nt;
+
+  const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
+  const bf16_t* a_src[NQ];
+  const bf16_t* bd_src[NQ];
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN / 2; ++tn) {
-        const int col = nt * (BN / 2) + wn * (WN / 2) + tn * 16 + col_in;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
-          if (mr < t.rows) {
-            const float gt = acc[tm][tn][r];
-            const float u = acc[tm][tn + TN / 2][r];
-            C[(t.row_begin + mr) * g.ldc + col] = f32_to_bf16(silu_f32(gt) * u);
-          }
-        }
-      }
-  } else if constexpr (MODE == MODE_DOWN) {
-    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int col = nt * BN + wn * WN + tn * 16 + col_in;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
-          if (mr < t.rows) C[(t.row_begin + mr) * g.ldc + col] = f32_to_bf16(acc[tm][tn][r]);
-        }
-      }
-  } else {
-    float* C = static_cast<float*>(g.C) + blockIdx.y * p.split_c;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int col = nt * BN + wn * WN + tn * 16 + col_in;
-        if (col < g.N) {
-          const float b = p.bias ? p.bias[col] : 0.f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
-            if (mr < t.rows) C[(t.row_begin + mr) * g.ldc + col] = acc[tm][tn][r] + b;
-          }
-        }
-      }
+  for (int i = 0; i < NQ; ++i) {
+    const int R = 8 * (wave * NQ + i) + lrow;
+    int mr = t.m_off + R;
+    mr = mr < t.rows ? mr : t.rows - 1;
+    a_src[i] = g.A + t.e * g.a_estride + (t.row_begin + mr) * g.lda + lchunk * 8;
+    if constexpr (!FP8)
+      bd_src[i] = static_cast<const bf16_t*>(g.B) + static_cast<size_t>(t.e) * g.b_estride +
+                  static_cast<size_t>(b_global_row<MODE, BN>(g, nt, R)) * g.ldb + lchunk * 8;
   }
+  const uint32_t lds_a = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) bf16_t*)(&sA[0][0])));
+  const uint32_t lds_b = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) bf16_t*)(&sB[0][0])));
+  auto issue = [&](int kt, int buf) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) lds_dma16(lds_a + buf * STAGE_BYTES + (wave * NQ + i) * 1024, a_src[i] + k0);
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) lds_dma16(lds_b + buf * STAGE_BYTES + (wave * NQ + i) * 1024, bd_src[i] + k0);
+    }
+  };
+
+  // fp8 weights: register path, as in gemm_tile
+  const uint8_t* b_src[CB];
+  int b_lds[CB], b_lds2[CB];
+  bool b_up[CB];
+  float scv[2][2] = {{1.f, 1.f}, {1.f, 1.f}};
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int c = tid + i * 256;
+      const int r = c / (BK / 16), kc = c % (BK / 16);
+      const int gr = b_global_row<MODE, BN>(g, nt, r);
+      b_up[i] = r >= BN / 2;
+      b_src[i] = static_cast<const uint8_t*>(g.B) + static_cast<size_t>(t.e) * g.b_estride +
+                 static_cast<size_t>(gr) * g.ldb + kc * 16;
+      b_lds[i] = lds_off_k<BK>(r, 2 * kc);
+      b_lds2[i] = lds_off_k<BK>(r, 2 * kc + 1);
+    }
+    const int kblocks = K / 128;
+    const float* se = g.bscale + static_cast<size_t>(t.e) * (g.b_rows / 128) * kblocks;
+    const float* srow0;
+    const float* srow1;
+    if constexpr (MODE == MODE_GATEUP) {
+      srow0 = se + static_cast<size_t>((nt * (BN / 2)) / 128) * kblocks;
+      srow1 = se + static_cast<size_t>((g.N + nt * (BN / 2)) / 128) * kblocks;
+    } else {
+      srow0 = se + static_cast<size_t>((nt * BN) / 128) * kblocks;
+      srow1 = srow0;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float* row = j == 0 ? srow0 : srow1;
+      scv[j][0] = row[min(lane, kblocks - 1)];
+      scv[j][1] = row[min(lane + 64, kblocks - 1)];
+    }
+  }
+  u32x4_t rb0[CB > 0 ? CB : 1], rb1[CB > 0 ? CB : 1];
+  float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};
+  auto load_b = [&](int kt, u32x4_t* rb, float* sc) {
+    if constexpr (FP8) {
+      const int k0 = kt * BK;
+#pragma unroll
+      for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + k0);
+      const int blk = k0 / 128;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float v = blk < 64 ? scv[j][0] : scv[j][1];
+        sc[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), blk & 63));
+      }
+    }
+  };
+  auto store_b = [&](int buf, const u32x4_t* rb, const float* sc) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        u32x4_t lo, hi;
+        fp8x16_to_bf16x16(rb[i], (MODE == MODE_GATEUP && b_up[i]) ? sc[1] : sc[0], lo, hi);
+        *reinterpret_cast<u32x4_t*>(&sB[buf][b_lds[i]]) = lo;
+        *reinterpret_cast<u32x4_t*>(&sB[buf][b_lds2[i]]) = hi;
+      }
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int frag_row = lane & 15, frag_c = lane >> 4;
+  const int tm_valid = __builtin_amdgcn_readfirstlane(
+      max(0, min(TM, (t.rows - t.m_off - wm * WM + 15) / 16)));
+  auto compute = [&](int buf, auto full) {
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      bf16x8_t af[TM], bfv[TN];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        if (decltype(full)::value || tm < tm_valid)
+          af[tm] = *reinterpret_cast<const bf16x8_t*>(
+              &sA[buf][lds_off_k<BK>(wm * WM + tm * 16 + frag_row, kk * 4 + frag_c)]);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        bfv[tn] = *reinterpret_cast<const bf16x8_t*>(
+            &sB[buf][lds_off_k<BK>(b_lds_row<MODE, WN, TN, BN>(wn, tn) + frag_row, kk * 4 + frag_c)]);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        if (decltype(full)::value || tm < tm_valid)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfv[tn], acc[tm][tn], 0, 0, 0);
+    }
+  };
+
+  // prologue: stage 0 in LDS buffer 0; fp8 weights of stage 1 in slot 1
+  load_b(0, rb0, sc0);
+  if (KT > 1) load_b(1, rb1, sc1);
+  issue(0, 0);
+  store_b(0, rb0, sc0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  // one stage; slot `cur` (0 or 1) is free once stage kt was stored
+  auto stage = [&](int kt, int buf, u32x4_t* rb_cur, float* sc_cur, u32x4_t* rb_next, float* sc_next,
+                   auto full) {
+    if (kt + 1 < KT) issue(kt + 1, buf ^ 1);
+    if (kt + 2 < KT) load_b(kt + 2, rb_cur, sc_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(buf, full);
+    if (kt + 1 < KT) store_b(buf ^ 1, rb_next, sc_next);
+    if (FP8 && kt + 2 < KT)
+      wait_vmcnt<CB>();                   // only the weight loads of stage kt + 2 may be in flight
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+  };
+  using Full = std::integral_constant<bool, true>;
+  using Part = std::integral_constant<bool, false>;
+  int kt = 0;
+  if (tm_valid == TM) {
+    for (; kt + 1 < KT; kt += 2) {
+      stage(kt, 0, rb0, sc0, rb1, sc1, Full{});
+      stage(kt + 1, 1, rb1, sc1, rb0, sc0, Full{});
+    }
+    if (kt < KT) stage(kt, 0, rb0, sc0, rb1, sc1, Full{});
+  } else {
+    for (; kt + 1 < KT; kt += 2) {
+      stage(kt, 0, rb0, sc0, rb1, sc1, Part{});
+      stage(kt + 1, 1, rb1, sc1, rb0, sc0, Part{});
+    }
+    if (kt < KT) stage(kt, 0, rb0, sc0, rb1, sc1, Part{});
+  }
+  store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc);
 }
 
 // Waves per SIMD each tile shape is built for: 4 for the 32-row tile with
@@ -552,6 +774,19 @@ __global__ __launch_bounds__(256, (MinWaves<BM, BK>::value)) void k_gemm_nt(Gemm
     gemm_tile<BM, WAVES_M, WAVES_N, MODE, FP8, BN, BK>(p.g[0], t, p, sA, sB);
   else
     gemm_tile<BM, WAVES_M, WAVES_N, MODE, false, BN, BK>(p.g[t.grp], t, p, sA, sB);
+}
+
+// The 128-row tiles with DMA staging (group 0 only: a launch without a dense
+// group of shared experts).
+template <int MODE, bool FP8>
+__global__ __launch_bounds__(256, 2) void k_gemm_dma(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][128 * kBK];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kBN * kBK];
+  int* s_loc = reinterpret_cast<int*>(&sA[0][0]);
+  TileLoc t;
+  if (!locate_tile<128>(p, s_loc, t)) return;
+  __syncthreads();                                  // s_loc read by all before sA is filled
+  gemm_tile_dma<MODE, FP8>(p.g[0], t, p, sA, sB);
 }
 
 // Worst-case number of row tiles: sum_e ceil(n_e / BM) <= ceil(cap / BM) + E_loc.
