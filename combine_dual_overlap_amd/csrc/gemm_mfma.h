@@ -86,7 +86,7 @@ struct TileShape {
   static constexpr int WN = BN / WAVES_N;
   static constexpr int TM = WM / 16;
   static constexpr int TN = WN / 16;
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
+  static_assert(WAVES_M * WAVES_N == 4 || WAVES_M * WAVES_N == 8, "4 or 8 waves per workgroup");
   static_assert(TM >= 1 && TN >= 2 && TN % 2 == 0, "wave tile shape");
 };
 
@@ -233,10 +233,18 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(const u32x4_t& q, float s, u32
 
 // Epilogue of a tile: gate/up applies SiLU(gate) * up and rounds h to bf16;
 // down rounds y to bf16; the router writes fp32 logits (+ bias).
+// bf16 outputs go through LDS (`scratch`, the tile's free activation buffers,
+// at least BM x BN bf16): each wave writes its block row-major with the
+// 16-byte chunks of a row XOR-swizzled by the row, then reads it back 16 bytes
+// per lane and stores whole 16-byte pieces of output rows.  An accumulator
+// lane holds 4 rows of one column, so storing straight from the registers
+// takes one 2-byte store per element (measured: the Qwen3-shaped down GEMM
+// spent a quarter of its time on them).
 template <int BM, int WAVES_M, int WAVES_N, int MODE, int BN>
 __device__ __forceinline__ void store_tile(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
                                            const f32x4_t (&acc)[TileShape<BM, WAVES_M, WAVES_N, BN>::TM]
-                                                                [TileShape<BM, WAVES_M, WAVES_N, BN>::TN]) {
+                                                                [TileShape<BM, WAVES_M, WAVES_N, BN>::TN],
+                                           bf16_t* scratch) {
   using S = TileShape<BM, WAVES_M, WAVES_N, BN>;
   constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
   const int lane = threadIdx.x & 63;
@@ -244,41 +252,9 @@ __device__ __forceinline__ void store_tile(const GemmGroup& g, const TileLoc& t,
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   const int nt = t.nt;
-  // Epilogue.  Accumulator element r of lane l in a 16x16 tile is
-  // (row 4*(l/16) + r, column l%16).
   const int col_in = lane & 15;
   const int row_q = (lane >> 4) * 4;
-  if constexpr (MODE == MODE_GATEUP) {
-    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN / 2; ++tn) {
-        const int col = nt * (BN / 2) + wn * (WN / 2) + tn * 16 + col_in;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
-          if (mr < t.rows) {
-            const float gt = acc[tm][tn][r];
-            const float u = acc[tm][tn + TN / 2][r];
-            C[(t.row_begin + mr) * g.ldc + col] = f32_to_bf16(silu_f32(gt) * u);
-          }
-        }
-      }
-  } else if constexpr (MODE == MODE_DOWN) {
-    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int col = nt * BN + wn * WN + tn * 16 + col_in;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int mr = t.m_off + wm * WM + tm * 16 + row_q + r;
-          if (mr < t.rows) C[(t.row_begin + mr) * g.ldc + col] = f32_to_bf16(acc[tm][tn][r]);
-        }
-      }
-  } else {
+  if constexpr (MODE == MODE_ROUTER) {
     float* C = static_cast<float*>(g.C) + blockIdx.y * p.split_c;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -294,6 +270,42 @@ __device__ __forceinline__ void store_tile(const GemmGroup& g, const TileLoc& t,
           }
         }
       }
+  } else {
+    constexpr int OW = MODE == MODE_GATEUP ? WN / 2 : WN;     // output columns of a wave
+    constexpr int OT = OW / 16;                                // 16-column MFMA tiles of it
+    constexpr int CPR = OW / 8;                                // 16-byte chunks per output row
+    static_assert(CPR >= 2 && (CPR & (CPR - 1)) == 0, "epilogue chunking");
+    bf16_t* W = scratch + wave * WM * OW;
+    auto woff = [](int r, int c) { return r * OW + (((c >> 3) ^ (r & (CPR - 1))) << 3) + (c & 7); };
+    __syncthreads();                              // every wave is done reading the stage buffers
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < OT; ++tn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v;
+          if constexpr (MODE == MODE_GATEUP)
+            v = silu_f32(acc[tm][tn][r]) * acc[tm][tn + TN / 2][r];
+          else
+            v = acc[tm][tn][r];
+          W[woff(tm * 16 + row_q + r, tn * 16 + col_in)] = f32_to_bf16(v);
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    bf16_t* C = static_cast<bf16_t*>(g.C) + t.e * g.c_estride;
+    const int col0 = MODE == MODE_GATEUP ? nt * (BN / 2) + wn * OW : nt * BN + wn * OW;
+#pragma unroll
+    for (int i = 0; i < (WM * CPR + 63) / 64; ++i) {
+      const int ch = lane + 64 * i;
+      if (WM * CPR % 64 != 0 && ch >= WM * CPR) break;
+      const int rr = ch / CPR, cc = ch % CPR;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&W[rr * OW + ((cc ^ (rr & (CPR - 1))) << 3)]);
+      const int mr = t.m_off + wm * WM + rr;
+      if (mr < t.rows)
+        *reinterpret_cast<u32x4_t*>(&C[(t.row_begin + mr) * g.ldc + col0 + cc * 8]) = v;
+    }
   }
 }
 
@@ -548,7 +560,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
     compute_stage(0);
   }
 
-  store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc);
+  store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc, &sA[0][0]);
 }
 
 // One LDS DMA (global_load_lds_dwordx4): each lane's 16 bytes land at
@@ -752,7 +764,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmGroup& g, const TileLoc&
     }
     if (kt < KT) stage(kt, 0, rb0, sc0, rb1, sc1, Part{});
   }
-  store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc);
+  store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc, &sA[0][0]);
 }
 
 // Waves per SIMD each tile shape is built for: 4 for the 32-row tile with
