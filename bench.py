@@ -34,9 +34,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
-KERNEL_SOURCES = ["combine_dual_overlap_amd/csrc/gemm_mfma.h", "combine_dual_overlap_amd/csrc/gemm_wstream.h",
-                  "combine_dual_overlap_amd/csrc/gemm_fp8.h", "combine_dual_overlap_amd/csrc/fp8_act.h",
-                  "combine_dual_overlap_amd/csrc/ffn.hip"]
+KERNEL_SOURCES = ["combine_dual_overlap_amd/csrc/gemm_mfma.h", "combine_dual_overlap_amd/csrc/gemm_fp8.h",
+                  "combine_dual_overlap_amd/csrc/fp8_act.h", "combine_dual_overlap_amd/csrc/ffn.hip"]
 
 
 def log(*a):
@@ -420,7 +419,7 @@ def main():
     ap.add_argument("--trial-steps", type=int, default=20, help="steps per trial")
     ap.add_argument("--comm-cu-budget", type=int, default=0)
     ap.add_argument("--ffn-tile-m", type=int, default=0,
-                    help="expert FFN row tile: 0 automatic, 16 weight-streaming kernel, 32/64/128 LDS-tiled kernel")
+                    help="expert FFN row tile: 0 automatic, else 32, 64 or 128 rows")
     ap.add_argument("--fp8-act", action="store_true",
                     help="routed experts with fp8 activations (fp8-weight configurations 3 and 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -564,7 +563,8 @@ def main():
             (64 if m + 3 * m ** 0.5 + 1 <= 64 else 128)
     kname = ("k_gemm_nt_f32 (fp32 SIMT)" if cfg.act == "f32" else
              f"k_gemm_f8 ({tile}-row LDS tiles, fp8 x fp8)" if args.fp8_act else
-             "k_gemm_ws (weight-streaming, 16-row tiles)" if tile == 16 else f"k_gemm_nt ({tile}-row LDS tiles)")
+             "k_gemm_dma (128-row tiles staged by LDS DMA)" if (tile == 128 and cfg.wdt == "bf16" and not I_sh) else
+             f"k_gemm_nt ({tile}-row LDS tiles)")
     roof["kernel"] = f"gate/up expert GEMM + SwiGLU, routed and shared experts: {kname}, MODE_GATEUP"
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
     roof["algorithmic_bytes_per_launch"] = int(bytes_launch)

@@ -141,8 +141,6 @@ moe_status check_ffn_shapes(moe_dtype act, moe_dtype wdt, int32_t H, int32_t I, 
 // K chunks of a dense (shared) expert's down projection run in the grouped
 // launch: each chunk writes its own partial output slab [rows1, H].
 int dense_down_chunks(moe_dtype act, int32_t I1, int32_t I);
-// True if the weight-streaming GEMM (16-row tiles) can run every GEMM of a call.
-bool ffn_ws_fits(moe_dtype act, int32_t H, int32_t I, int64_t rows1, int32_t I1);
 size_t ffn_ws_bytes(int64_t cap_rows, int32_t I, moe_dtype act);
 
 struct CombineArgs {

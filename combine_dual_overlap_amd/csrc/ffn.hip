@@ -11,7 +11,6 @@
 #include <cmath>
 
 #include "gemm_fp8.h"
-#include "gemm_wstream.h"
 
 namespace dbomoe {
 
@@ -19,10 +18,7 @@ namespace dbomoe {
 // the row tile for the likely largest expert, so most experts take one row
 // tile (their weights stream once) and large experts get the big MFMA tile.
 // Measured on the five layer shapes (DBO schedule): 32-row tiles for decode,
-// 64 up to about 96 rows, 128 beyond.  The weight-streaming kernel (16-row
-// tiles) is faster in isolation when every expert holds at most 16 rows, but
-// splits the Poisson tail of 17-32-row experts into two tiles, and loses to
-// the 32-row LDS-tiled kernel inside the layer; it is used only on request.
+// 64 up to about 96 rows, 128 beyond.
 static int choose_tile_m(int64_t mean_rows) {
   const double m = static_cast<double>(mean_rows);
   const double est_max = m + 3.0 * std::sqrt(m) + 1.0;
@@ -31,7 +27,7 @@ static int choose_tile_m(int64_t mean_rows) {
   return 128;
 }
 
-// 16: weight-streaming kernel; 32/64/128: LDS-tiled kernel with that row tile.
+// Row tiles of 32, 64 or 128 rows.
 // The 32-row tile takes 64 weight rows per column tile (2 x 2 waves of 16 x
 // 32): twice the tiles of 128-row-wide columns, so the last partial round of
 // workgroups is shorter (decode gate/up with the shared experts 145.5 ->
@@ -59,9 +55,7 @@ static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g) {
     hipLaunchKernelGGL((k_gemm_dma<MODE, false>), grid, dim3(256), 0, s, g);
     return;
   }
-  if (bm == 16)
-    hipLaunchKernelGGL((k_gemm_ws<MODE, FP8>), grid, dim3(kWsWaves * kWave), 0, s, g);
-  else if (bm == 32 && k_multiple_of(g, 2 * kBK))
+  if (bm == 32 && k_multiple_of(g, 2 * kBK))
     hipLaunchKernelGGL((k_gemm_nt<32, 2, 2, MODE, FP8, 64, 2 * kBK>), grid, dim3(256), 0, s, g);
   else if (bm == 32)
     hipLaunchKernelGGL((k_gemm_nt<32, 2, 2, MODE, FP8, 64>), grid, dim3(256), 0, s, g);
@@ -148,14 +142,6 @@ static int64_t tiles_max(int bm, int64_t cap_rows, int E_loc, bool dense, int n_
   const int64_t rt1 = rows1 > 0 ? (rows1 + bm - 1) / bm : 0;
   const int64_t rt0 = cap_rows > 0 ? max_row_tiles(cap_rows, E_loc, bm, dense) : 0;
   return rt0 * n_tiles0 + E1 * rt1 * n_tiles1;
-}
-
-// True if every GEMM of the call has K <= kWsKMax (the weight-streaming
-// kernel keeps the whole K of its activation tile in LDS).
-bool ffn_ws_fits(moe_dtype act, int32_t H, int32_t I, int64_t rows1, int32_t I1) {
-  if (act == MOE_F32 || H > kWsKMax || I > kWsKMax) return false;
-  if (rows1 > 0 && I1 / dense_down_chunks(act, I1, I) > kWsKMax) return false;
-  return true;
 }
 
 // ---- fp8 activations ------------------------------------------------------
@@ -276,7 +262,6 @@ moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.act == MOE_F32) return launch_ffn_f32(a, s);
   const bool fp8 = a.wdt == MOE_FP8_E4M3FN;
   const bool dense = a.offsets == nullptr;
-  if (a.tile_m == 16 && !ffn_ws_fits(a.act, a.H, a.I, a.rows1, a.I1)) return MOE_ERR_UNSUPPORTED;
   const int bm = a.tile_m > 0 ? a.tile_m : choose_tile_m(a.rows_hint);
 
   GemmParams p1{};
@@ -435,8 +420,7 @@ extern "C" moe_status moe_grouped_ffn(const void* x_perm, moe_dtype act, int32_t
   if (st != MOE_OK) return st;
   if (cap_rows < 0) return MOE_ERR_INVALID_ARG;
   if (!offsets && E_loc != 1) return MOE_ERR_INVALID_ARG;
-  if (tile_m != 0 && tile_m != 16 && tile_m != 32 && tile_m != 64 && tile_m != 128) return MOE_ERR_INVALID_ARG;
-  if (tile_m == 16 && !ffn_ws_fits(act, H, I, 0, 0)) return MOE_ERR_UNSUPPORTED;
+  if (tile_m != 0 && tile_m != 32 && tile_m != 64 && tile_m != 128) return MOE_ERR_INVALID_ARG;
   if (cap_rows == 0) return MOE_OK;
   if (cap_rows > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (!x_perm || !w13 || !w2 || !y_perm || !ws) return MOE_ERR_INVALID_ARG;

@@ -363,11 +363,8 @@ extern "C" moe_status dbo_moe_layer(dbo_ctx* ctx, const moe_layer_desc* d, const
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (o->schedule < DBO_SCHED_UNSPLIT || o->schedule > DBO_SCHED_DBO_RECV_HOOK) return MOE_ERR_INVALID_ARG;
   if (o->min_tokens_to_split < 0 || o->comm_cu_budget < 0) return MOE_ERR_INVALID_ARG;
-  if (o->ffn_tile_m != 0 && o->ffn_tile_m != 16 && o->ffn_tile_m != 32 && o->ffn_tile_m != 64 &&
-      o->ffn_tile_m != 128)
+  if (o->ffn_tile_m != 0 && o->ffn_tile_m != 32 && o->ffn_tile_m != 64 && o->ffn_tile_m != 128)
     return MOE_ERR_INVALID_ARG;
-  if (o->ffn_tile_m == 16 && !ffn_ws_fits(d->act, d->H, d->I, d->shared_I > 0 ? 1 : 0, d->shared_I))
-    return MOE_ERR_UNSUPPORTED;
   if (d->fp8_act && o->ffn_tile_m != 0 && o->ffn_tile_m != 64 && o->ffn_tile_m != 128) return MOE_ERR_UNSUPPORTED;
   if (o->split_at != -1 && (o->split_at < 1 || o->split_at >= T)) return MOE_ERR_INVALID_ARG;
   for (auto& v : ctx->stats) v = 0;

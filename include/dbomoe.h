@@ -209,9 +209,8 @@ moe_status moe_get_device_error(const void* dispatch_ws, int32_t* code, void* st
  *            per-128x128-block scales for fp8 (real W = code value * scale);
  *            must be NULL otherwise
  *   y_perm   [cap_rows, H] out, act; rows >= offsets[E_loc] untouched
- *   tile_m   0 = automatic; 16 = the weight-streaming kernel (16-row tiles,
- *            H and I <= 2048, else MOE_ERR_UNSUPPORTED); 32, 64 or 128 = the
- *            LDS-tiled kernel with that many rows per tile
+ *   tile_m   0 = automatic; 32, 64 or 128 rows per tile; any other value
+ *            MOE_ERR_INVALID_ARG
  *   ws       moe_ffn_workspace_size(cap_rows, I, act) bytes (holds h)
  * H % 128 == 0 and I % 64 == 0 (fp8: I % 128 == 0), else MOE_ERR_UNSUPPORTED.
  * fp8 weights are expanded to bf16 (code value x block scale, rounded once) on
@@ -222,8 +221,7 @@ size_t moe_ffn_workspace_size(int64_t cap_rows, int32_t I, moe_dtype act);
  * rows_per_expert rows (dbo_moe_layer passes ceil(T*k/E)); rows1/I1 describe
  * a dense group run in the same launches (the shared experts of
  * dbo_moe_layer: rows1 = microbatch tokens, I1 = shared_I), 0/0 if none.
- * Returns 32, 64 or 128 (LDS-tiled kernel; the automatic choice never takes
- * the weight-streaming kernel), or 0 for shapes moe_grouped_ffn rejects.
+ * Returns 32, 64 or 128, or 0 for shapes moe_grouped_ffn rejects.
  * Pure host function. */
 int32_t moe_ffn_auto_tile(moe_dtype act, moe_dtype wdt, int32_t H, int32_t I, int64_t rows_per_expert,
                           int64_t rows1, int32_t I1);

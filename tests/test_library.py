@@ -110,9 +110,9 @@ def test_entry_points_reject_bad_arguments_without_a_device():
     # tile height out of range
     assert L.moe_grouped_ffn(A, B.MOE_BF16, 256, 192, A, 4, 100, A, A, B.MOE_BF16, None, None, A, 48, A,
                              1 << 30, None) == B.MOE_ERR_INVALID_ARG
-    # the weight-streaming kernel keeps K <= 2048 of its activation tile in LDS
+    # 16-row tiles are not offered
     assert L.moe_grouped_ffn(A, B.MOE_BF16, 4096, 192, A, 4, 100, A, A, B.MOE_BF16, None, None, A, 16, A,
-                             1 << 30, None) == B.MOE_ERR_UNSUPPORTED
+                             1 << 30, None) == B.MOE_ERR_INVALID_ARG
     # combine: out aliasing y_perm
     assert L.moe_combine(A, B.MOE_BF16, 4, 128, 2, A, A, None, A, None) == B.MOE_ERR_INVALID_ARG
     # route: group-limited with k larger than the kept groups hold
