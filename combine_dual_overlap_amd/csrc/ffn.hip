@@ -11,6 +11,7 @@
 #include <cmath>
 
 #include "gemm_fp8.h"
+#include "gemm_fp8w.h"
 
 namespace dbomoe {
 
@@ -47,12 +48,22 @@ static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g) {
   // bf16 weights, 128-row tiles, no dense group: activation and weight tiles
   // staged by LDS DMA (bitwise equal to the register-staged kernel; measured
   // standalone on the skewed-layer shapes: gate/up 401 -> 367 us, down 217 ->
-  // 197 us).  fp8 weights keep the register path: their expansion needs the
-  // registers anyway, and the compiler's load accounting would force every
-  // hand-counted DMA issued before a register load, so only the activation
-  // DMA would stay one stage ahead (measured: no gain).
+  // 197 us).
   if (!FP8 && bm == 128 && g.rows1 == 0 && g.g[0].K % kBK == 0) {
     hipLaunchKernelGGL((k_gemm_dma<MODE, false>), grid, dim3(256), 0, s, g);
+    return;
+  }
+  // fp8 weights, 64- or 128-row tiles, no dense group: fp8 codes staged by LDS
+  // DMA, converted exactly at fragment read, block scales applied to the fp32
+  // block sums (gemm_fp8w.h).  Measured standalone against the register path
+  // (which expands value(code) x scale to bf16 before LDS): Qwen3-shaped
+  // prefill gate/up 373.8 -> 310.2 us, down 229.1 -> 206.2 us; R1-shaped share
+  // gate/up (K = 7168, 64-row tiles) 333.5 -> 283.3 us.
+  if (FP8 && (bm == 64 || bm == 128) && g.rows1 == 0 && g.g[0].K / 128 <= kW8MaxKBlocks) {
+    if (bm == 128)
+      hipLaunchKernelGGL((k_gemm_fp8w<MODE, 128>), grid, dim3(256), 0, s, g);
+    else
+      hipLaunchKernelGGL((k_gemm_fp8w<MODE, 64>), grid, dim3(256), 0, s, g);
     return;
   }
   if (bm == 32 && k_multiple_of(g, 2 * kBK))
