@@ -5,8 +5,8 @@
 //
 // Every operand is staged by LDS DMA (global_load_lds_dwordx4, counted by
 // hand): activation rows as bf16, weight rows as their fp8 codes, in a ring of
-// three 64-wide K stages, so two stages are in flight while the MFMAs of the
-// third run, and no register ring or LDS store sits on the load path.
+// 64-wide K stages (three: two stages are in flight while the MFMAs of the
+// third run), and no register ring or LDS store sits on the load path.
 //
 // The weights stay fp8 in LDS.  Each wave converts its fragments exactly to
 // bf16 when it reads them (every e4m3 value is a bf16 value) and the MFMAs sum
@@ -21,8 +21,8 @@
 // both steps.  A reduction is the same sum in any order of its terms.
 //
 // Tile: BM (64 or 128) rows x 128 weight rows (gate/up: 64 gate + the 64
-// matching up rows), 2 x 2 waves, each a (BM/2) x 64 block of 16x16x32 bf16
-// MFMAs.  Group 0 (routed experts) only.
+// matching up rows), WAVES_M x WAVES_N waves (2 x 2 or 2 x 4), each a block of
+// 16x16x32 bf16 MFMAs.  Group 0 (routed experts) only.
 #pragma once
 
 #include "gemm_mfma.h"
@@ -51,35 +51,50 @@ __device__ __forceinline__ void fp8x16_to_bf16_exact(const u32x4_t& c, bf16x8_t&
   hi = __builtin_bit_cast(bf16x8_t, u32x4_t{o[4], o[5], o[6], o[7]});
 }
 
-constexpr int kW8Buf = 3;                                      // LDS stages in the ring
-template <int BM> struct W8Lds {
+// K blocks of one tile's scale rows (one 64-lane dword DMA per row)
+constexpr int kW8MaxKBlocks = 64;
+template <int BM, int NBUF> struct W8Lds {
   static constexpr int A = BM * kBK * 2;                       // activation stage
   static constexpr int B = kBN * kBK;                          // fp8 weight stage
-  static constexpr int bytes = kW8Buf * (A + B);               // 72 KB (BM 128), 48 KB (BM 64)
+  static constexpr int S = 2 * kW8MaxKBlocks * 4;              // two scale rows
+  static constexpr int bytes = NBUF * (A + B) + S;
 };
-// K blocks a wave can hold scales for (two per lane)
-constexpr int kW8MaxKBlocks = 128;
 
-template <int MODE, int BM>
+// Waits until at most n stages of this wave's DMAs (NDMA each) are in flight.
+template <int NDMA, int MAXN>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN * NDMA>();
+      return;
+    }
+    wait_stages<NDMA, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+template <int MODE, int BM, int WAVES_M, int WAVES_N, int NBUF>
 __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
                                                uint8_t* lds) {
-  constexpr int BN = kBN, BK = kBK, WAVES_M = 2, WAVES_N = 2;
+  constexpr int BN = kBN, BK = kBK, NW = WAVES_M * WAVES_N;
   using S = TileShape<BM, WAVES_M, WAVES_N, BN>;
   constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
-  constexpr int A_BYTES = W8Lds<BM>::A, B_BYTES = W8Lds<BM>::B;
-  constexpr int NQA = BM / 8 / 4;            // activation DMAs per wave per stage (8 rows each)
-  constexpr int NQB = BN / 16 / 4;           // weight DMAs per wave per stage (16 rows each)
+  constexpr int A_BYTES = W8Lds<BM, NBUF>::A, B_BYTES = W8Lds<BM, NBUF>::B;
+  constexpr int NQA = BM / 8 / NW;           // activation DMAs per wave per stage (8 rows each)
+  constexpr int NQB = BN / 16 / NW;          // weight DMAs per wave per stage (16 rows each)
   constexpr int NDMA = NQA + NQB;
-  static_assert(NQA >= 1 && NQB >= 1 && NDMA < 16, "DMA split");
+  static_assert(NQA >= 1 && NQB >= 1 && NQA * NW * 8 == BM && NQB * NW * 16 == BN, "DMA split");
+  static_assert(NBUF >= 3 && (NBUF - 2) * NDMA < 64, "ring depth");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int K = g.K, KT = K / BK, nt = t.nt;
 
   uint8_t* sA = lds;
-  uint8_t* sB = lds + kW8Buf * A_BYTES;
+  uint8_t* sB = lds + NBUF * A_BYTES;
   const uint32_t lds_a = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(lds)));
-  const uint32_t lds_b = lds_a + kW8Buf * A_BYTES;
+  const uint32_t lds_b = lds_a + NBUF * A_BYTES;
 
   // Activation DMA i of this wave fills tile rows 8 (wave NQA + i) .. + 7:
   // lane l takes row l / 8 of the group and its 16-byte chunk (l % 8) ^ (l / 8),
@@ -103,7 +118,9 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
                static_cast<size_t>(b_global_row<MODE, BN>(g, nt, r)) * g.ldb + qlog * 16;
   }
   // Block scales of this column tile: the gate and up row blocks (or the one
-  // row block of a down tile), K block j in lane j % 64 of slot j / 64.
+  // row block of a down tile), staged into LDS by wave 0 ahead of the first
+  // stage (one dword DMA per row, lane j carrying K block j), so they arrive
+  // with the first stage instead of costing a memory round trip of their own.
   const int kblocks = K / 128;
   const float* se = g.bscale + static_cast<size_t>(t.e) * (g.b_rows / 128) * kblocks;
   const float* srow0;
@@ -115,16 +132,15 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
     srow0 = se + static_cast<size_t>((nt * BN) / 128) * kblocks;
     srow1 = srow0;
   }
-  float scv[2][2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float* row = j == 0 ? srow0 : srow1;
-    scv[j][0] = row[min(lane, kblocks - 1)];
-    scv[j][1] = row[min(lane + 64, kblocks - 1)];
-  }
+  const float* sS = reinterpret_cast<const float*>(lds + NBUF * (A_BYTES + B_BYTES));
   // Every load the compiler issued has completed: inside the loop only the
   // DMAs are in flight, and their waits are counted by hand.
   __builtin_amdgcn_s_waitcnt(0);
+  if (wave == 0) {
+    const uint32_t lds_s = lds_a + NBUF * (A_BYTES + B_BYTES);
+    lds_dma4(lds_s, srow0 + min(lane, kblocks - 1));
+    lds_dma4(lds_s + kW8MaxKBlocks * 4, srow1 + min(lane, kblocks - 1));
+  }
 
   auto issue = [&](int kt, int buf) {
     const int k0 = kt * BK;
@@ -177,12 +193,7 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   };
   // acc += s * blk for K block kb
   auto scale_block = [&](int kb, auto full) {
-    float s[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float v = kb < 64 ? scv[j][0] : scv[j][1];
-      s[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kb & 63));
-    }
+    const float s[2] = {sS[kb], sS[kW8MaxKBlocks + kb]};
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
       if (decltype(full)::value || tm < tm_valid)
@@ -194,38 +205,34 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
         }
   };
 
-  // Ring: stage kt lives in buffer kt % 3.  Stage kt issues the DMAs of stage
-  // kt + 2 into the buffer stage kt - 1 used (every wave left it at the
-  // previous barrier), runs its MFMAs, waits for its own DMAs of stage kt + 1
-  // (those of kt + 2 may stay in flight) and meets the others at the barrier.
-  issue(0, 0);
-  if (KT > 1) issue(1, 1);
-  if (KT > 1)
-    wait_vmcnt<NDMA>();
-  else
-    wait_vmcnt<0>();
+  // Ring of NBUF stages: stage kt lives in buffer kt % NBUF.  Stage kt issues
+  // the DMAs of stage kt + NBUF - 1 into the buffer stage kt - 1 used (every
+  // wave left it at the previous barrier), runs its MFMAs, waits for its own
+  // DMAs of stage kt + 1 (later stages may stay in flight) and meets the
+  // other waves at the barrier.  The wait before the first stage also covers
+  // wave 0's scale DMAs, which were issued before any stage.
+  const int pre = min(NBUF - 1, KT);
+  for (int s = 0; s < pre; ++s) issue(s, s);
+  wait_stages<NDMA, NBUF - 2>(pre - 1);
   __syncthreads();
-  auto stage = [&](int kt, int buf, int buf2, auto first, auto full) {
-    if (kt + 2 < KT) issue(kt + 2, buf2);
+  auto stage = [&](int kt, int buf, auto first, auto full) {
+    const int ahead = kt + NBUF - 1;
+    if (ahead < KT) issue(ahead, buf == 0 ? NBUF - 1 : buf - 1);
     compute(buf, first, full);
     if (!decltype(first)::value) scale_block(kt >> 1, full);
-    if (kt + 2 < KT)
-      wait_vmcnt<NDMA>();
-    else
-      wait_vmcnt<0>();
+    wait_stages<NDMA, NBUF - 2>(min(KT - 1, ahead) - (kt + 1));
     __syncthreads();
   };
   using True = std::integral_constant<bool, true>;
   using False = std::integral_constant<bool, false>;
   // KT is even (K is a multiple of 128): two stages per K block.
   auto run = [&](auto full) {
-    int buf = 0;                               // kt % 3
+    int buf = 0;                               // kt % NBUF
     for (int kt = 0; kt < KT; kt += 2) {
-      const int b1 = buf == 2 ? 0 : buf + 1, b2 = b1 == 2 ? 0 : b1 + 1;
-      stage(kt, buf, b2, True{}, full);        // stage kt + 2 goes to (kt + 2) % 3 = b2
-      const int b3 = b2 == 2 ? 0 : b2 + 1;
-      stage(kt + 1, b1, b3, False{}, full);
-      buf = b2;
+      const int b1 = buf == NBUF - 1 ? 0 : buf + 1;
+      stage(kt, buf, True{}, full);
+      stage(kt + 1, b1, False{}, full);
+      buf = b1 == NBUF - 1 ? 0 : b1 + 1;
     }
   };
   if (tm_valid == TM)
@@ -235,16 +242,26 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc, reinterpret_cast<bf16_t*>(sA));
 }
 
+// Waves per SIMD a shape runs at: workgroups per CU from its LDS (160 KB per
+// CU) times its waves, over 4 SIMDs (at most 4: the register budget of a wave
+// is 512 / waves per SIMD).
+template <int BM, int NW, int NBUF> struct W8Occ {
+  static constexpr int wgs = (160 * 1024) / W8Lds<BM, NBUF>::bytes;
+  static constexpr int w = wgs * NW / 4;
+  static constexpr int value = w < 1 ? 1 : w > 4 ? 4 : w;
+};
+
 // Group 0 only (a launch without a dense group of shared experts); K a
 // multiple of 128 with at most kW8MaxKBlocks blocks.
-template <int MODE, int BM>
-__global__ __launch_bounds__(256, (BM == 128 ? 2 : 3)) void k_gemm_fp8w(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[W8Lds<BM>::bytes];
+template <int MODE, int BM, int WAVES_M = 2, int WAVES_N = 2, int NBUF = 3>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, (W8Occ<BM, WAVES_M * WAVES_N, NBUF>::value))
+void k_gemm_fp8w(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[W8Lds<BM, NBUF>::bytes];
   int* s_loc = reinterpret_cast<int*>(lds);
   TileLoc t;
   if (!locate_tile<BM>(p, s_loc, t)) return;
   __syncthreads();                                  // s_loc read by all before the ring is filled
-  gemm_tile_fp8w<MODE, BM>(p.g[0], t, p, lds);
+  gemm_tile_fp8w<MODE, BM, WAVES_M, WAVES_N, NBUF>(p.g[0], t, p, lds);
 }
 
 }  // namespace dbomoe

@@ -100,17 +100,22 @@ template <int BM>
 __device__ __forceinline__ bool locate_tile(const GemmParams& p, int* s_loc, TileLoc& t) {
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    int t4[4];
+    int t4[4], o4[4], n4[4];
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ex = lane * 4 + i;
-      int n = 0;
+      int n = 0, o = 0;
       if (p.offsets) {
-        if (ex < p.E_loc) n = p.offsets[ex + 1] - p.offsets[ex];
+        if (ex < p.E_loc) {
+          o = p.offsets[ex];
+          n = p.offsets[ex + 1] - o;
+        }
       } else if (ex == 0) {
         n = static_cast<int>(p.dense_rows);
       }
+      o4[i] = o;
+      n4[i] = n;
       t4[i] = (n + BM - 1) / BM;
       sum += t4[i];
     }
@@ -151,6 +156,8 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int* s_loc, Til
             s_loc[2] = lane * 4 + i;
             s_loc[3] = local % t4[i];
             s_loc[4] = local / t4[i];
+            s_loc[5] = o4[i];          // the expert's first row and row count, so
+            s_loc[6] = n4[i];          // no workgroup reads the offsets twice
           }
           acc += t4[i];
         }
@@ -167,8 +174,8 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int* s_loc, Til
     t.row_begin = 0;
     t.rows = static_cast<int>(p.rows1);
   } else if (p.offsets) {
-    t.row_begin = p.offsets[t.e];
-    t.rows = p.offsets[t.e + 1] - p.offsets[t.e];
+    t.row_begin = s_loc[5];
+    t.rows = s_loc[6];
   } else {
     t.row_begin = 0;
     t.rows = static_cast<int>(p.dense_rows);
@@ -573,9 +580,18 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gptr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(gptr) : "memory");
 }
 
+// s_waitcnt vmcnt(N): vmcnt is 6 bits, its low 4 in bits 3:0 and its high 2
+// in bits 15:14; expcnt (6:4) and lgkmcnt (11:8) at their maxima, not waited for.
+// One 4-byte LDS DMA (global_load_lds_dword): lane l's word lands at
+// lds_addr + 4 * lane.
+__device__ __forceinline__ void lds_dma4(uint32_t lds_addr, const void* gptr) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(a), "v"(gptr) : "memory");
+}
+
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0xF70 | N);      // vmcnt(N); expcnt and lgkmcnt not waited for
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // The 128 x 128 tile of gemm_tile with its activation rows staged by LDS DMA
