@@ -58,15 +58,15 @@ static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g) {
   // block sums (gemm_fp8w.h).  Measured standalone against the register path
   // (which expands value(code) x scale to bf16 before LDS): Qwen3-shaped
   // prefill gate/up 373.8 -> 310.2 us, down 229.1 -> 206.2 us; R1-shaped share
-  // gate/up (K = 7168, 64-row tiles) 333.5 -> 283.3 us.  The down GEMMs (short
-  // K, many column tiles) run 8 waves per tile, 2 x 4, at 4 waves per SIMD
-  // (Qwen3-shaped 204.0 -> 191.1 us, R1-shaped 151.8 -> 141.0 us); for gate/up
-  // 2 x 2 stays faster (308.2 against 329.7 us).
+  // gate/up (K = 7168, 64-row tiles) 333.5 -> 283.3 us.  The 128-row down
+  // GEMM (short K, many column tiles) runs 8 waves per tile, 2 x 4, at 4 waves
+  // per SIMD: Qwen3-shaped prefill down 193 -> 178 us in the layer.  2 x 2
+  // stays faster for gate/up (308.2 against 329.7 us standalone) and for the
+  // 64-row down tiles of the R1-shaped share in the layer (148.5 against
+  // 166.7 us, although 141.5 against 154.5 us standalone).
   if (FP8 && (bm == 64 || bm == 128) && g.rows1 == 0 && g.g[0].K / 128 <= kW8MaxKBlocks) {
     if (MODE == MODE_DOWN && bm == 128)
       hipLaunchKernelGGL((k_gemm_fp8w<MODE, 128, 2, 4>), grid, dim3(512), 0, s, g);
-    else if (MODE == MODE_DOWN)
-      hipLaunchKernelGGL((k_gemm_fp8w<MODE, 64, 2, 4>), grid, dim3(512), 0, s, g);
     else if (bm == 128)
       hipLaunchKernelGGL((k_gemm_fp8w<MODE, 128>), grid, dim3(256), 0, s, g);
     else
