@@ -564,6 +564,8 @@ def main():
     kname = ("k_gemm_nt_f32 (fp32 SIMT)" if cfg.act == "f32" else
              f"k_gemm_f8 ({tile}-row LDS tiles, fp8 x fp8)" if args.fp8_act else
              "k_gemm_dma (128-row tiles staged by LDS DMA)" if (tile == 128 and cfg.wdt == "bf16" and not I_sh) else
+             f"k_gemm_fp8w ({tile}-row tiles, fp8 codes staged by LDS DMA)" if (tile in (64, 128) and cfg.wdt == "fp8"
+                                                                              and not I_sh) else
              f"k_gemm_nt ({tile}-row LDS tiles)")
     roof["kernel"] = f"gate/up expert GEMM + SwiGLU, routed and shared experts: {kname}, MODE_GATEUP"
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
