@@ -26,3 +26,26 @@ def read_golden(name):
             key, *vals = line.split()
             out[key] = vals
     return out
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Parity margins of the run: for every passing tolerance check, its worst
+    elementwise error in units of its bound and its relative RMS error in
+    units of its tolerance (1.0 = at the bound)."""
+    helpers = sys.modules.get("helpers")
+    rows = getattr(helpers, "MARGINS", None)
+    if not rows:
+        return
+    tr = terminalreporter
+    tr.section("parity margins (fraction of the bound used)")
+    worst_by_test = {}
+    for test, what, m_el, m_rms in rows:
+        k = test or "?"
+        w = worst_by_test.get(k)
+        if w is None or max(m_el, m_rms) > max(w[1], w[2]):
+            worst_by_test[k] = (what, m_el, m_rms)
+    for test in sorted(worst_by_test):
+        what, m_el, m_rms = worst_by_test[test]
+        tr.write_line(f"{m_el:6.3f} elementwise  {m_rms:6.3f} rel-RMS  {test}  [{what}]")
+    top = max(max(m_el, m_rms) for _, _, m_el, m_rms in rows)
+    tr.write_line(f"{len(rows)} checks; largest fraction of a bound used: {top:.3f}")
