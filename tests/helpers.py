@@ -14,16 +14,21 @@ import workloads as W
 #  * elementwise, relative to the magnitude of what each element sums:
 #    |gpu - ref| <= tol * (A + rms(A)/100), with A the oracle's per-element sum
 #    of |terms| (for the layer: sum_j |w_j| (|h_j| |W2|^T), plus the shared
-#    experts).  The GPU rounds h, y_perm and out to bf16 once each; the
+#    experts).  bf16 keeps an 8-bit significand, so one rounding errs by at
+#    most u = 2^-8 relative.  The GPU rounds h, y_perm and out once each; the
 #    register-staged fp8 tiles (32-row tiles, launches with a dense group)
-#    round an fp8 weight once more (code value times its block scale, to
-#    bf16), the DMA-staged ones never do: a first-order error of at most
-#    4 * 2^-9 * A (0.8 % of A), so tol = 1e-2 holds for bf16 and fp8 weights
-#    alike, even where the weighted expert outputs cancel;
+#    round each weight once more (code value times its block scale, to bf16),
+#    the DMA-staged ones never do.  The y_perm and out roundings contribute at
+#    most u * A each; the h and weight roundings enter through sums over the
+#    intermediate (or K) dimension whose errors have independent signs
+#    (about u * A / sqrt(I)).  So about 2u * A = 0.8 % of A, and tol = 1e-2
+#    holds for bf16 and fp8 weights alike, even where the weighted expert
+#    outputs cancel (the strict worst case, every rounding aligned, would be
+#    3u-4u * A);
 #  * over the whole output, relative to the output:
 #    ||gpu - ref||_2 <= tol * ||ref||_2 (the "rel" reading of the layer's
-#    statement).  Independent roundings of relative size <= 2^-9 give a
-#    relative RMS error near 2^-9 / sqrt(3) per rounding, about 0.1 %.
+#    statement).  Independent roundings of relative size <= 2^-8 give a
+#    relative RMS error near 2^-8 / sqrt(3) per rounding, about 0.2 %.
 # The layer's statement allows 1e-2 (bf16) and 5e-2 (fp8 weights); both
 # checks use 1e-2 for fp8 weights too, which the bound above supports.
 # fp32 (tiny config): 1e-4.  Without a scale the elementwise rule falls back
