@@ -168,6 +168,9 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   // MFMAs of one stage into the block accumulator (FIRST: the block's first
   // stage, whose first step starts from zero).
   auto compute = [&](int buf, auto first, auto full) {
+    // a wave with no rows in this tile (the last row tile of an expert) only
+    // stages its share of the DMAs and meets the barriers
+    if (!decltype(full)::value && tm_valid == 0) return;
     const bf16_t* A = reinterpret_cast<const bf16_t*>(sA + buf * A_BYTES);
     const uint8_t* B = sB + buf * B_BYTES;
     bf16x8_t blo[TN], bhi[TN];
@@ -193,6 +196,7 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   };
   // acc += s * blk for K block kb
   auto scale_block = [&](int kb, auto full) {
+    if (!decltype(full)::value && tm_valid == 0) return;
     const float s[2] = {sS[kb], sS[kW8MaxKBlocks + kb]};
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)

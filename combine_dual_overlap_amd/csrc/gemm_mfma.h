@@ -464,6 +464,7 @@ __device__ __forceinline__ void gemm_tile(const GemmGroup& g, const TileLoc& t, 
   const int tm_valid = __builtin_amdgcn_readfirstlane(
       max(0, min(TM, (t.rows - t.m_off - wm * WM + 15) / 16)));
   auto compute_stage = [&](int buf) {
+    if (tm_valid == 0) return;            // no rows for this wave in this tile
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       bf16x8_t af[TM], bfv[TN];
@@ -722,6 +723,7 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmGroup& g, const TileLoc&
   const int tm_valid = __builtin_amdgcn_readfirstlane(
       max(0, min(TM, (t.rows - t.m_off - wm * WM + 15) / 16)));
   auto compute = [&](int buf, auto full) {
+    if (!decltype(full)::value && tm_valid == 0) return;   // no rows for this wave
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       bf16x8_t af[TM], bfv[TN];
