@@ -35,7 +35,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 KERNEL_SOURCES = ["combine_dual_overlap_amd/csrc/gemm_mfma.h", "combine_dual_overlap_amd/csrc/gemm_fp8.h",
-                  "combine_dual_overlap_amd/csrc/fp8_act.h", "combine_dual_overlap_amd/csrc/ffn.hip"]
+                  "combine_dual_overlap_amd/csrc/gemm_fp8w.h", "combine_dual_overlap_amd/csrc/fp8_act.h",
+                  "combine_dual_overlap_amd/csrc/ffn.hip"]
 
 
 def log(*a):
@@ -543,7 +544,7 @@ def main():
     dn_roof = float(np.mean([r[0] for r in roofs["down"]]))
     mfma_part = float(np.mean([r[3] for r in roofs["gate_up"]]))
     hbm_bound = mfma_part < gu_roof / 2        # the bound that holds most of the per-expert roof
-    traffic = read_traffic(f"c{args.config}" + ("_fp8act" if args.fp8_act else ""))
+    traffic = read_traffic(cfg.name + ("_fp8act" if args.fp8_act else ""))
     ach_gbs = bytes_launch / avg_s / 1e9
     ach_tf = flops_launch / avg_s / 1e12
     if hbm_bound:
