@@ -45,12 +45,12 @@ static bool k_multiple_of(const GemmParams& g, int bk) {
 
 template <int MODE, bool FP8>
 static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g) {
-  // bf16 weights, 128-row tiles, no dense group: activation and weight tiles
-  // staged by LDS DMA (bitwise equal to the register-staged kernel; measured
+  // bf16 weights, 128-row tiles: activation and weight tiles staged by LDS
+  // DMA (bitwise equal to the register-staged kernel; measured
   // standalone on the skewed-layer shapes: gate/up 401 -> 367 us, down 217 ->
   // 197 us).
-  if (!FP8 && bm == 128 && g.rows1 == 0 && g.g[0].K % kBK == 0) {
-    hipLaunchKernelGGL((k_gemm_dma<MODE, false>), grid, dim3(256), 0, s, g);
+  if (!FP8 && bm == 128 && k_multiple_of(g, kBK)) {
+    hipLaunchKernelGGL((k_gemm_dma<MODE>), grid, dim3(256), 0, s, g);
     return;
   }
   // fp8 weights, 64- or 128-row tiles, no dense group: fp8 codes staged by LDS

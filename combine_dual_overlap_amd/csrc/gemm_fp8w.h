@@ -60,20 +60,6 @@ template <int BM, int NBUF> struct W8Lds {
   static constexpr int bytes = NBUF * (A + B) + S;
 };
 
-// Waits until at most n stages of this wave's DMAs (NDMA each) are in flight.
-template <int NDMA, int MAXN>
-__device__ __forceinline__ void wait_stages(int n) {
-  if constexpr (MAXN > 0) {
-    if (n >= MAXN) {
-      wait_vmcnt<MAXN * NDMA>();
-      return;
-    }
-    wait_stages<NDMA, MAXN - 1>(n);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-
 template <int MODE, int BM, int WAVES_M, int WAVES_N, int NBUF>
 __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
                                                uint8_t* lds) {

@@ -595,123 +595,89 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
 }
 
-// The 128 x 128 tile of gemm_tile with its activation rows staged by LDS DMA
-// (and bf16 weight rows too): no register ring and no LDS stores for them.
-// A synthetic stage probe on MI355X (128 x 128 tile, 64-wide K stages, two
+// Waits until at most n stages of this wave's DMAs (NDMA each) are in flight.
+template <int NDMA, int MAXN>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN * NDMA>();
+      return;
+    }
+    wait_stages<NDMA, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// gemm_tile with both operands staged by LDS DMA (bf16 activations and bf16
+// weights): no register ring and no LDS stores sit on the load path.  A
+// synthetic stage probe on MI355X (128 x 128 tile, 64-wide K stages, two
 // workgroups per CU, L2-resident data) ran 1.05-1.16 PFLOP/s with register
-// staging and LDS stores and 1.41-1.52 PFLOP/s with DMA staging.  fp8 weights
-// still take the register path: each code is expanded once, value(code)
-// times its block scale rounded to bf16, and stored to LDS (the same
-// arithmetic as gemm_tile, so the outputs are bitwise equal).
-// Each 8-row group of a stage is one DMA: lane l carries row l / 8 of the
-// group and that row's 16-byte chunk (l % 8) ^ (l / 8), so the chunks land in
-// the XOR-swizzled order the fragment reads expect.
-// Schedule per stage kt (LDS buffer kt % 2): issue the DMA of stage kt + 1
-// into the other buffer and the fp8 weight loads of stage kt + 2 into the
-// register slot just freed; MFMAs of stage kt; expand and store the fp8
-// weights of stage kt + 1; wait for this wave's DMA of stage kt + 1 (vmcnt:
-// at most the newer weight loads may still be in flight); barrier.
-template <int MODE, bool FP8>
+// staging and LDS stores and 1.41-1.52 PFLOP/s with DMA staging.  The same
+// arithmetic as gemm_tile, so the outputs are bitwise equal.
+// A stage is BK wide (CPR = BK / 8 16-byte chunks per row); each DMA fills
+// 64 / CPR rows: lane l carries row R = first row + l / CPR and that row's
+// chunk (l % CPR) ^ (R & 7), so the chunks land in the XOR-swizzled order
+// the fragment reads expect.  Ring of NBUF stages (stage kt in buffer kt % NBUF):
+// stage kt issues stage kt + NBUF - 1 into the buffer stage kt - 1 used,
+// computes, waits for this wave's DMAs of stage kt + 1 and meets the others
+// at the barrier.  ROT: each weight tile walks K from its own starting stage
+// (the 32-row decode tiles, as gemm_tile does).
+template <int BM, int BN, int BK, int NBUF> struct DmaLds {
+  static constexpr int A = BM * BK * 2, B = BN * BK * 2, bytes = NBUF * (A + B);
+};
+
+template <int MODE, int BM, int BN, int BK, int NBUF, bool ROT>
 __device__ __forceinline__ void gemm_tile_dma(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
-                                              bf16_t (*sA)[128 * kBK], bf16_t (*sB)[128 * kBK]) {
-  constexpr int BM = 128, BN = kBN, BK = kBK, WAVES_M = 2, WAVES_N = 2;
+                                              uint8_t* lds) {
+  constexpr int WAVES_M = 2, WAVES_N = 2;
   using S = TileShape<BM, WAVES_M, WAVES_N, BN>;
   constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
-  constexpr int NQ = BM / 8 / 4;                  // 8-row DMA groups per wave per stage
-  constexpr int CB = BN * (BK / 16) / 256;        // fp8: 16-byte weight chunks per thread per stage
-  constexpr int STAGE_BYTES = BM * BK * 2;
-  static_assert(BN == BM, "A and B DMA groups share the row mapping");
+  constexpr int CPR = BK / 8, RPD = 64 / CPR;            // chunks per row, rows per DMA
+  constexpr int NQA = BM / RPD / 4, NQB = BN / RPD / 4;  // DMAs per wave per stage
+  constexpr int NDMA = NQA + NQB;
+  constexpr int A_BYTES = DmaLds<BM, BN, BK, NBUF>::A, B_BYTES = DmaLds<BM, BN, BK, NBUF>::B;
+  static_assert(NQA >= 1 && NQB >= 1 && NQA * 4 * RPD == BM && NQB * 4 * RPD == BN, "DMA split");
+  static_assert(NBUF >= 2 && (NBUF - 2) * NDMA < 64, "ring");
+  static_assert(4 * WM * (MODE == MODE_GATEUP ? WN / 2 : WN) * 2 <= NBUF * A_BYTES, "epilogue scratch");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int K = g.K, KT = K / BK, nt = t.nt;
+  const int kt_rot = ROT ? __builtin_amdgcn_readfirstlane(rotation_start(t.e * g.n_tiles + t.nt, KT)) : 0;
 
-  const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
-  const bf16_t* a_src[NQ];
-  const bf16_t* bd_src[NQ];
+  uint8_t* sA = lds;
+  uint8_t* sB = lds + NBUF * A_BYTES;
+  const uint32_t lds_a = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(lds)));
+  const uint32_t lds_b = lds_a + NBUF * A_BYTES;
+
+  // the swizzle takes the tile row R (a DMA's first row is a multiple of RPD,
+  // which is not a multiple of 8 for 128-wide stages)
+  const int lrow = lane / CPR, lpos = lane % CPR;
+  const bf16_t* a_src[NQA];
+  const bf16_t* b_src[NQB];
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int R = 8 * (wave * NQ + i) + lrow;
+  for (int i = 0; i < NQA; ++i) {
+    const int R = RPD * (wave * NQA + i) + lrow;
     int mr = t.m_off + R;
     mr = mr < t.rows ? mr : t.rows - 1;
-    a_src[i] = g.A + t.e * g.a_estride + (t.row_begin + mr) * g.lda + lchunk * 8;
-    if constexpr (!FP8)
-      bd_src[i] = static_cast<const bf16_t*>(g.B) + static_cast<size_t>(t.e) * g.b_estride +
-                  static_cast<size_t>(b_global_row<MODE, BN>(g, nt, R)) * g.ldb + lchunk * 8;
+    a_src[i] = g.A + t.e * g.a_estride + (t.row_begin + mr) * g.lda + (lpos ^ (R & 7)) * 8;
   }
-  const uint32_t lds_a = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) bf16_t*)(&sA[0][0])));
-  const uint32_t lds_b = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) bf16_t*)(&sB[0][0])));
-  auto issue = [&](int kt, int buf) {
-    const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) lds_dma16(lds_a + buf * STAGE_BYTES + (wave * NQ + i) * 1024, a_src[i] + k0);
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) lds_dma16(lds_b + buf * STAGE_BYTES + (wave * NQ + i) * 1024, bd_src[i] + k0);
-    }
-  };
-
-  // fp8 weights: register path, as in gemm_tile
-  const uint8_t* b_src[CB];
-  int b_lds[CB], b_lds2[CB];
-  bool b_up[CB];
-  float scv[2][2] = {{1.f, 1.f}, {1.f, 1.f}};
-  if constexpr (FP8) {
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int c = tid + i * 256;
-      const int r = c / (BK / 16), kc = c % (BK / 16);
-      const int gr = b_global_row<MODE, BN>(g, nt, r);
-      b_up[i] = r >= BN / 2;
-      b_src[i] = static_cast<const uint8_t*>(g.B) + static_cast<size_t>(t.e) * g.b_estride +
-                 static_cast<size_t>(gr) * g.ldb + kc * 16;
-      b_lds[i] = lds_off_k<BK>(r, 2 * kc);
-      b_lds2[i] = lds_off_k<BK>(r, 2 * kc + 1);
-    }
-    const int kblocks = K / 128;
-    const float* se = g.bscale + static_cast<size_t>(t.e) * (g.b_rows / 128) * kblocks;
-    const float* srow0;
-    const float* srow1;
-    if constexpr (MODE == MODE_GATEUP) {
-      srow0 = se + static_cast<size_t>((nt * (BN / 2)) / 128) * kblocks;
-      srow1 = se + static_cast<size_t>((g.N + nt * (BN / 2)) / 128) * kblocks;
-    } else {
-      srow0 = se + static_cast<size_t>((nt * BN) / 128) * kblocks;
-      srow1 = srow0;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float* row = j == 0 ? srow0 : srow1;
-      scv[j][0] = row[min(lane, kblocks - 1)];
-      scv[j][1] = row[min(lane + 64, kblocks - 1)];
-    }
+  for (int i = 0; i < NQB; ++i) {
+    const int R = RPD * (wave * NQB + i) + lrow;
+    b_src[i] = static_cast<const bf16_t*>(g.B) + static_cast<size_t>(t.e) * g.b_estride +
+               static_cast<size_t>(b_global_row<MODE, BN>(g, nt, R)) * g.ldb + (lpos ^ (R & 7)) * 8;
   }
-  u32x4_t rb0[CB > 0 ? CB : 1], rb1[CB > 0 ? CB : 1];
-  float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};
-  auto load_b = [&](int kt, u32x4_t* rb, float* sc) {
-    if constexpr (FP8) {
-      const int k0 = kt * BK;
+  __builtin_amdgcn_s_waitcnt(0);     // only hand-counted DMAs in flight from here
+  auto issue = [&](int kt) {
+    int ks = kt + kt_rot;
+    ks = ks >= KT ? ks - KT : ks;
+    const int k0 = ks * BK, buf = kt % NBUF;
 #pragma unroll
-      for (int i = 0; i < CB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + k0);
-      const int blk = k0 / 128;
+    for (int i = 0; i < NQA; ++i) lds_dma16(lds_a + buf * A_BYTES + (wave * NQA + i) * 1024, a_src[i] + k0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float v = blk < 64 ? scv[j][0] : scv[j][1];
-        sc[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), blk & 63));
-      }
-    }
-  };
-  auto store_b = [&](int buf, const u32x4_t* rb, const float* sc) {
-    if constexpr (FP8) {
-#pragma unroll
-      for (int i = 0; i < CB; ++i) {
-        u32x4_t lo, hi;
-        fp8x16_to_bf16x16(rb[i], (MODE == MODE_GATEUP && b_up[i]) ? sc[1] : sc[0], lo, hi);
-        *reinterpret_cast<u32x4_t*>(&sB[buf][b_lds[i]]) = lo;
-        *reinterpret_cast<u32x4_t*>(&sB[buf][b_lds2[i]]) = hi;
-      }
-    }
+    for (int i = 0; i < NQB; ++i) lds_dma16(lds_b + buf * B_BYTES + (wave * NQB + i) * 1024, b_src[i] + k0);
   };
 
   f32x4_t acc[TM][TN];
@@ -722,20 +688,21 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmGroup& g, const TileLoc&
   const int frag_row = lane & 15, frag_c = lane >> 4;
   const int tm_valid = __builtin_amdgcn_readfirstlane(
       max(0, min(TM, (t.rows - t.m_off - wm * WM + 15) / 16)));
-  auto compute = [&](int buf, auto full) {
+  auto compute = [&](int kt, auto full) {
     if (!decltype(full)::value && tm_valid == 0) return;   // no rows for this wave
+    const bf16_t* A = reinterpret_cast<const bf16_t*>(sA + (kt % NBUF) * A_BYTES);
+    const bf16_t* B = reinterpret_cast<const bf16_t*>(sB + (kt % NBUF) * B_BYTES);
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
       bf16x8_t af[TM], bfv[TN];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
         if (decltype(full)::value || tm < tm_valid)
-          af[tm] = *reinterpret_cast<const bf16x8_t*>(
-              &sA[buf][lds_off_k<BK>(wm * WM + tm * 16 + frag_row, kk * 4 + frag_c)]);
+          af[tm] = *reinterpret_cast<const bf16x8_t*>(&A[lds_off_k<BK>(wm * WM + tm * 16 + frag_row, kk * 4 + frag_c)]);
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
         bfv[tn] = *reinterpret_cast<const bf16x8_t*>(
-            &sB[buf][lds_off_k<BK>(b_lds_row<MODE, WN, TN, BN>(wn, tn) + frag_row, kk * 4 + frag_c)]);
+            &B[lds_off_k<BK>(b_lds_row<MODE, WN, TN, BN>(wn, tn) + frag_row, kk * 4 + frag_c)]);
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
         if (decltype(full)::value || tm < tm_valid)
@@ -745,44 +712,24 @@ __device__ __forceinline__ void gemm_tile_dma(const GemmGroup& g, const TileLoc&
     }
   };
 
-  // prologue: stage 0 in LDS buffer 0; fp8 weights of stage 1 in slot 1
-  load_b(0, rb0, sc0);
-  if (KT > 1) load_b(1, rb1, sc1);
-  issue(0, 0);
-  store_b(0, rb0, sc0);
-  wait_vmcnt<0>();
+  const int pre = min(NBUF - 1, KT);
+  for (int s = 0; s < pre; ++s) issue(s);
+  wait_stages<NDMA, NBUF - 2>(pre - 1);
   __syncthreads();
-  // one stage; slot `cur` (0 or 1) is free once stage kt was stored
-  auto stage = [&](int kt, int buf, u32x4_t* rb_cur, float* sc_cur, u32x4_t* rb_next, float* sc_next,
-                   auto full) {
-    if (kt + 1 < KT) issue(kt + 1, buf ^ 1);
-    if (kt + 2 < KT) load_b(kt + 2, rb_cur, sc_cur);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(buf, full);
-    if (kt + 1 < KT) store_b(buf ^ 1, rb_next, sc_next);
-    if (FP8 && kt + 2 < KT)
-      wait_vmcnt<CB>();                   // only the weight loads of stage kt + 2 may be in flight
-    else
-      wait_vmcnt<0>();
+  auto stage = [&](int kt, auto full) {
+    if (kt + NBUF - 1 < KT) issue(kt + NBUF - 1);
+    compute(kt, full);
+    wait_stages<NDMA, NBUF - 2>(min(KT - 1, kt + NBUF - 1) - (kt + 1));
     __syncthreads();
   };
   using Full = std::integral_constant<bool, true>;
   using Part = std::integral_constant<bool, false>;
-  int kt = 0;
   if (tm_valid == TM) {
-    for (; kt + 1 < KT; kt += 2) {
-      stage(kt, 0, rb0, sc0, rb1, sc1, Full{});
-      stage(kt + 1, 1, rb1, sc1, rb0, sc0, Full{});
-    }
-    if (kt < KT) stage(kt, 0, rb0, sc0, rb1, sc1, Full{});
+    for (int kt = 0; kt < KT; ++kt) stage(kt, Full{});
   } else {
-    for (; kt + 1 < KT; kt += 2) {
-      stage(kt, 0, rb0, sc0, rb1, sc1, Part{});
-      stage(kt + 1, 1, rb1, sc1, rb0, sc0, Part{});
-    }
-    if (kt < KT) stage(kt, 0, rb0, sc0, rb1, sc1, Part{});
+    for (int kt = 0; kt < KT; ++kt) stage(kt, Part{});
   }
-  store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc, &sA[0][0]);
+  store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc, reinterpret_cast<bf16_t*>(sA));
 }
 
 // Waves per SIMD each tile shape is built for: 4 for the 32-row tile with
@@ -806,17 +753,16 @@ __global__ __launch_bounds__(256, (MinWaves<BM, BK>::value)) void k_gemm_nt(Gemm
     gemm_tile<BM, WAVES_M, WAVES_N, MODE, false, BN, BK>(p.g[t.grp], t, p, sA, sB);
 }
 
-// The 128-row tiles with DMA staging (group 0 only: a launch without a dense
-// group of shared experts).
-template <int MODE, bool FP8>
-__global__ __launch_bounds__(256, 2) void k_gemm_dma(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][128 * kBK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kBN * kBK];
-  int* s_loc = reinterpret_cast<int*>(&sA[0][0]);
+// bf16 tiles with DMA staging; both groups (a dense group of shared experts
+// runs through the same tile).
+template <int MODE, int BM = 128, int BN = kBN, int BK = kBK, int NBUF = 2, bool ROT = false, int MINW = 2>
+__global__ __launch_bounds__(256, MINW) void k_gemm_dma(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DmaLds<BM, BN, BK, NBUF>::bytes];
+  int* s_loc = reinterpret_cast<int*>(lds);
   TileLoc t;
-  if (!locate_tile<128>(p, s_loc, t)) return;
-  __syncthreads();                                  // s_loc read by all before sA is filled
-  gemm_tile_dma<MODE, FP8>(p.g[0], t, p, sA, sB);
+  if (!locate_tile<BM>(p, s_loc, t)) return;
+  __syncthreads();                                  // s_loc read by all before the ring is filled
+  gemm_tile_dma<MODE, BM, BN, BK, NBUF, ROT>(p.g[t.grp], t, p, lds);
 }
 
 // Worst-case number of row tiles: sum_e ceil(n_e / BM) <= ceil(cap / BM) + E_loc.

@@ -319,6 +319,28 @@ def test_bf16_row_tiles_agree(cid):
     agree(ys, "H=2048 I=1408")
 
 
+@pytest.mark.parametrize("cid", [3, 4])
+def test_fp8_weight_row_tiles_agree(cid):
+    """fp8 weights: the DMA-staged tiles of 64 and 128 rows (gate/up 2 x 2
+    waves; down 2 x 2 and 2 x 4 waves) add the same fp32 block sums, each
+    scaled by its block scale with one fma, in the same K order, so their
+    outputs are equal bit for bit.  (Each tile, and the register-staged
+    32-row tile that rounds the weights first, is checked against the oracle
+    by test_grouped_ffn.)"""
+    C = _gpu()
+    inp, ov = inputs(cid, True)
+    cfg = inp["cfg"]
+    ids = O.moe_layer_expert(ov, tokens=np.arange(1))["ids"]
+    ref = O.dispatch_ref(ids, cfg.expert_begin, cfg.expert_end)
+    x_perm = inp["x"][torch.from_numpy(ref["perm"] // cfg.k).long()].contiguous().cuda()
+    off = torch.from_numpy(ref["offsets"]).cuda()
+    args = (cfg.I, off, cfg.E_loc, inp["w13"].cuda(), inp["w2"].cuda(), inp["w13_scale"].cuda(),
+            inp["w2_scale"].cuda())
+    y64, y128 = (_ffn(C, x_perm, *args, tile_m=tm)[:ref["M"]] for tm in (64, 128))
+    assert torch.isfinite(y64.float()).all()
+    assert torch.equal(y64.view(torch.int16), y128.view(torch.int16)), "64 vs 128 rows"
+
+
 @pytest.mark.parametrize("cid", CIDS)
 def test_combine(cid):
     C = _gpu()
