@@ -416,7 +416,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, help="layer configuration 1..5 (default 3)")
-    ap.add_argument("--rounds", type=int, default=9, help="interleaved trial rounds per schedule")
+    ap.add_argument("--rounds", type=int, default=10, help="interleaved trial rounds per schedule")
     ap.add_argument("--trial-steps", type=int, default=20, help="steps per trial")
     ap.add_argument("--comm-cu-budget", type=int, default=0)
     ap.add_argument("--ffn-tile-m", type=int, default=0,
