@@ -22,14 +22,20 @@
 //  * 4 waves; each wave owns a WM x WN block made of 16x16 MFMA tiles
 //    (v_mfma_f32_16x16x32_bf16, fp32 accumulators).  K advances BK per stage
 //    (64; 128 for the 32-row decode tile when K allows).
-//    Global loads run two stages ahead of the MFMAs (a two-deep register ring)
-//    and land in a double-buffered LDS tile (one barrier per stage).  LDS rows
-//    are 128 bytes with the 16-byte chunks XOR-swizzled by row, so the 16 rows
-//    an MFMA fragment read touches fall in distinct banks without padding (the
-//    32-row tile then fits four workgroups per CU).
-//  * fp8 e4m3 weights are expanded on their way to LDS: code value times its
-//    128x128 block scale, rounded once to bf16 (the stage's 64- or 128-wide K slice lies
-//    in one scale block, and so do the 64 gate or 64 up rows of a tile).
+//  * Two ways to stage a K slice.  gemm_tile: global loads run two stages
+//    ahead of the MFMAs in a register ring and are stored into a
+//    double-buffered LDS tile (one barrier per stage).  gemm_tile_dma: LDS DMA
+//    (global_load_lds_dwordx4) writes the slices straight into a ring of LDS
+//    buffers.  Either way LDS rows are BK elements with the 16-byte chunks
+//    XOR-swizzled by row, so the rows an MFMA fragment read touches spread over
+//    the banks without padding.
+//  * The epilogue stages each wave's outputs through LDS and stores whole
+//    16-byte pieces of output rows.
+//  * fp8 e4m3 weights, on the register path, are expanded on their way to
+//    LDS: code value times its 128x128 block scale, rounded once to bf16 (the
+//    stage's K slice lies in one scale block, and so do the 64 gate or 64 up
+//    rows of a tile).  The 64- and 128-row fp8 tiles of routed experts use
+//    gemm_fp8w.h instead, which never rounds a weight.
 #pragma once
 
 #include <type_traits>
