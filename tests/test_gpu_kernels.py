@@ -341,6 +341,55 @@ def test_fp8_weight_row_tiles_agree(cid):
     assert torch.equal(y64.view(torch.int16), y128.view(torch.int16)), "64 vs 128 rows"
 
 
+def _fp8_experts(E, rows, cols, gen, zero_block_of=None):
+    """E expert matrices of block-quantised fp8 weights: N(0, 0.02) scaled by
+    2^u, u ~ U(-4, 4), per 128 x 128 block (so block scales differ), and one
+    all-zero block in expert zero_block_of."""
+    codes = torch.empty(E, rows, cols, dtype=torch.uint8)
+    scales = torch.empty(E, rows // 128, cols // 128, dtype=torch.float32)
+    for e in range(E):
+        u = (torch.rand(rows // 128, cols // 128, generator=gen) * 8.0 - 4.0)
+        f = torch.pow(2.0, u).repeat_interleave(128, 0).repeat_interleave(128, 1)
+        w = torch.randn(rows, cols, generator=gen) * 0.02 * f
+        if e == zero_block_of:
+            w[:128, :128] = 0.0
+        codes[e], scales[e] = W.quantize_fp8_blocks(w)
+    return codes, scales
+
+
+def _fp8_ffn_vs_oracle(C, H, I, counts, tiles, seed):
+    gen = torch.Generator().manual_seed(seed)
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offsets[-1])
+    x = torch.randn(M, H, generator=gen).to(torch.bfloat16)
+    c13, s13 = _fp8_experts(E, 2 * I, H, gen, zero_block_of=min(2, E - 1))
+    c2, s2 = _fp8_experts(E, H, I, gen)
+    want, scale = O.grouped_ffn_ref(
+        O.decode(W.bits(x), "bf16"), offsets,
+        lambda e: (O.dequant_fp8_blocks(c13[e].numpy(), s13[e].numpy()),
+                   O.dequant_fp8_blocks(c2[e].numpy(), s2[e].numpy())), with_scale=True)
+    for tm in tiles:
+        y = _ffn(C, x.cuda(), I, torch.from_numpy(offsets).cuda(), E, c13.cuda(), c2.cuda(), s13.cuda(), s2.cuda(),
+                 tile_m=tm)
+        print(f"fp8-weight ffn H={H} I={I} counts={list(counts)} tile_m={tm}", flush=True)
+        assert_close(to_f64(y[:M]), want, 1e-2, f"fp8 weights H={H} I={I} tile_m={tm}", scale)
+
+
+def test_fp8_weight_ffn_ragged_experts():
+    """fp8 weights, bf16 activations, experts of 0, 1, 33, 64, 65, 128, 129 and
+    257 rows: partial last row tiles, waves without rows, several row tiles;
+    varied block scales and an all-zero weight block (scale 1)."""
+    _fp8_ffn_vs_oracle(_gpu(), 256, 256, np.array([1, 0, 33, 64, 65, 128, 129, 257]), (32, 64, 128), 21)
+
+
+def test_fp8_weight_ffn_k_beyond_dma_scale_rows():
+    """H = 8448 (66 scale blocks along K) is past the 64 K blocks the
+    DMA-staged fp8 tile stages per scale row: the gate/up GEMM falls back to the
+    register-staged fp8 tile, the down GEMM (K = I = 128) stays DMA-staged."""
+    _fp8_ffn_vs_oracle(_gpu(), 8448, 128, np.array([3, 130]), (128,), 22)
+
+
 @pytest.mark.parametrize("cid", CIDS)
 def test_combine(cid):
     C = _gpu()
