@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+F8_DMA_MAX_K = 4096  # longest K the fp8 x fp8 GEMM stages by LDS DMA (kF8DmaMaxK)
 KERNEL_SOURCES = ["combine_dual_overlap_amd/csrc/gemm_mfma.h", "combine_dual_overlap_amd/csrc/gemm_fp8.h",
                   "combine_dual_overlap_amd/csrc/gemm_fp8w.h", "combine_dual_overlap_amd/csrc/fp8_act.h",
                   "combine_dual_overlap_amd/csrc/ffn.hip"]
@@ -563,7 +564,8 @@ def main():
         tile = (128 if args.ffn_tile_m >= 128 else 64) if args.ffn_tile_m else \
             (64 if m + 3 * m ** 0.5 + 1 <= 64 else 128)
     kname = ("k_gemm_nt_f32 (fp32 SIMT)" if cfg.act == "f32" else
-             f"k_gemm_f8 ({tile}-row LDS tiles, fp8 x fp8)" if args.fp8_act else
+             (f"k_gemm_f8d ({tile}-row tiles staged by LDS DMA, fp8 x fp8)" if cfg.H <= F8_DMA_MAX_K else
+              f"k_gemm_f8 ({tile}-row LDS tiles, fp8 x fp8)") if args.fp8_act else
              "k_gemm_dma (128-row tiles staged by LDS DMA)" if (tile == 128 and cfg.wdt == "bf16" and not I_sh) else
              f"k_gemm_fp8w ({tile}-row tiles, fp8 codes staged by LDS DMA)" if (tile in (64, 128) and cfg.wdt == "fp8"
                                                                               and not I_sh) else
