@@ -9,11 +9,12 @@ activations), the stand-in for the 8192-token prefill benchmark of "[Perf]
 Fix DBO overlap: capture DeepEP event before yield" (Test Plan / Test Result).
 
 Prints one JSON line: `value` is the DBO step captured once in a HIP graph and
-replayed K times (after W warm-up replays, bracketed by device syncs).  Beside
+replayed K times (after W warm-up replays, bracketed by device syncs).  Before
 it, the schedules DBO, SERIAL, DBO_LATE_EVENT (the event recorded after the
 yield, the over-serialisation the page fixes) and UNSPLIT are timed as
 interleaved repeated trials, graph-replayed and eager, with median and p10/p90
-per schedule and per-round paired ratios; the roofline of the dominant kernel
+per schedule and per-round paired ratios (the trials also bring the chip to
+its clocks under load before the headline's timed replays); the roofline of the dominant kernel
 (the gate/up expert GEMM) against the per-expert roof; the dispatch and
 combine HBM fractions; the CPU oracle on a bounded sample; and the
 DeepSeek-V2-Lite-shaped decode layer as a secondary record.
@@ -479,6 +480,13 @@ def main():
         trace_steps(L, run, ["dbo", "serial", "dbo_late_event"], args.trace_steps, torch)
         return
 
+    # The schedule comparison first: interleaved trials of every schedule,
+    # graph-replayed and eager.  They also bring the chip to the clocks it
+    # holds under this load, which a few warm-up steps from idle do not.
+    schedules = ["dbo", "serial", "dbo_late_event", "unsplit"]
+    log(f"bench: {args.rounds} interleaved rounds x {args.trial_steps} steps of {schedules}, graph and eager")
+    trials = summarize_trials(schedule_trials(L, run, schedules, args.rounds, args.trial_steps, 3), T)
+
     # The headline: the DBO step captured once in a HIP graph (the whole step,
     # both streams and their events, one launch), W warm-up replays, then
     # exactly K timed replays bracketed by device syncs.
@@ -501,10 +509,6 @@ def main():
     torch.cuda.synchronize()
     dt_graph = time.perf_counter() - t0
     del g
-
-    schedules = ["dbo", "serial", "dbo_late_event", "unsplit"]
-    log(f"bench: {args.rounds} interleaved rounds x {args.trial_steps} steps of {schedules}, graph and eager")
-    trials = summarize_trials(schedule_trials(L, run, schedules, args.rounds, args.trial_steps, 3), T)
 
     # Kernel timing: events around each microbatch's gate/up and down GEMMs on
     # the compute stream (the stream they are launched on), over more steps of

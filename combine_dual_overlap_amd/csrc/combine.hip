@@ -104,6 +104,67 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4_t* __restrict__ y, 
   }
 }
 
+// The combine issued beside an FFN launch on the other stream.  A CU running
+// the gate/up GEMM holds two of its workgroups, which leave 64 VGPRs per SIMD
+// lane and no room for a workgroup of k_combine (up to 110 VGPRs): each of
+// those would wait for a GEMM workgroup to retire and then hold its slot.
+// This variant takes one 64-chunk block per wave and the source rows eight at
+// a time, with the row addresses and weights wave-uniform (scalar registers),
+// and is held to 64 VGPRs, so that a workgroup fits beside the GEMM's two.
+// The same products are summed in the same order as in k_combine, so the
+// output is bitwise the same.
+template <bool BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(64))) void k_combine_lean(
+    const u32x4_t* __restrict__ y, int64_t T, int row_chunks, int k, const int32_t* __restrict__ inv,
+    const float* __restrict__ w, const u32x4_t* __restrict__ shared, int n_shared, u32x4_t* __restrict__ out) {
+  constexpr int EPC = BF16 ? 8 : 4;
+  constexpr int G = 8;                // source rows loaded together
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nblk = (row_chunks + 63) / 64;
+  const int rows = k + n_shared;
+  const int64_t items = T * nblk;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * 4 + wave; it < items; it += nwaves) {
+    const int64_t t = it / nblk;
+    const int ci = static_cast<int>(it % nblk) * 64 + lane;
+    const bool in = ci < row_chunks;
+    const int my_pos = lane < k ? inv[t * k + lane] : -1;
+    const float my_w = lane < k ? w[t * k + lane] : 0.f;
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+    for (int j0 = 0; j0 < rows; j0 += G) {
+      float wt[G];
+      u32x4_t v[G];
+      unsigned used = 0;   // bit g: source row j0 + g exists (its load is issued)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int j = j0 + g;
+        const int pj = __builtin_amdgcn_readfirstlane(__shfl(my_pos, j < k ? j : 0, kWave));
+        const float wj =
+            __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__shfl(my_w, j < k ? j : 0, kWave))));
+        const u32x4_t* src = nullptr;
+        wt[g] = 1.f;
+        if (j < k) {
+          if (pj >= 0) src = y + static_cast<int64_t>(pj) * row_chunks;
+          wt[g] = wj;
+        } else if (j < rows) {
+          src = shared + (static_cast<int64_t>(j - k) * T + t) * row_chunks;
+        }
+        if (src) {
+          used |= 1u << g;
+          if (in) v[g] = src[ci];
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        if (used & (1u << g)) acc_chunk<BF16>(acc, v[g], wt[g]);
+    }
+    if (in) out[t * row_chunks + ci] = pack_chunk<BF16>(acc);
+  }
+}
+
 // Rows per token = k + shared slabs (at most 32).  Two chunks per lane when
 // there are enough tokens to fill the GPU, one otherwise.
 template <bool BF16>
@@ -132,10 +193,19 @@ moe_status launch_combine(const CombineArgs& a, hipStream_t s) {
   auto* out = static_cast<u32x4_t*>(a.out);
   const int nsh = sh ? (a.n_shared > 0 ? a.n_shared : 1) : 0;
   if (a.k + nsh > 32) return MOE_ERR_UNSUPPORTED;
-  if (a.act == MOE_BF16)
+  if (a.beside_ffn) {
+    int64_t blocks = (a.T * ((rc + 63) / 64) + 3) / 4;
+    if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
+    const dim3 g(static_cast<unsigned>(blocks));
+    if (a.act == MOE_BF16)
+      hipLaunchKernelGGL(k_combine_lean<true>, g, dim3(256), 0, s, y, a.T, rc, a.k, a.inv, a.w, sh, nsh, out);
+    else
+      hipLaunchKernelGGL(k_combine_lean<false>, g, dim3(256), 0, s, y, a.T, rc, a.k, a.inv, a.w, sh, nsh, out);
+  } else if (a.act == MOE_BF16) {
     launch_k<true>(a.k + nsh, a.T, rc, a.max_blocks, s, y, a.k, a.inv, a.w, sh, nsh, out);
-  else
+  } else {
     launch_k<false>(a.k + nsh, a.T, rc, a.max_blocks, s, y, a.k, a.inv, a.w, sh, nsh, out);
+  }
   DBOMOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -88,6 +88,7 @@ inline size_t dtype_size(moe_dtype d) {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+
 #define DBOMOE_CHECK_LAUNCH()                                  \
   do {                                                         \
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;   \
@@ -110,6 +111,8 @@ struct DispatchArgs {
   int32_t* counts; int32_t* offsets; int32_t* tile_offsets; int32_t* perm; int32_t* inv;
   void* x_perm; void* ws; int32_t max_blocks;
   uint8_t* x_scale;        // non-NULL: x_perm receives fp8 codes and x_scale the E8M0 bytes [rows][H/128]
+  bool beside_ffn;         // issued to run beside an FFN launch on the other stream: kernels that fit
+                           // into what the GEMM's resident workgroups leave free on a CU
 };
 size_t dispatch_ws_bytes(int64_t T, int32_t k, int32_t E_loc);
 moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s);
@@ -147,6 +150,7 @@ struct CombineArgs {
   const void* y; moe_dtype act; int64_t T; int32_t H; int32_t k;
   const int32_t* inv; const float* w; const void* shared; void* out; int32_t max_blocks;
   int32_t n_shared;        // slabs [n_shared][T, H] added with weight 1 (1 if shared is set)
+  bool beside_ffn;         // as in DispatchArgs
 };
 moe_status launch_combine(const CombineArgs& a, hipStream_t s);
 

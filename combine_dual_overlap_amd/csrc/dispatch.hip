@@ -320,6 +320,129 @@ __global__ __launch_bounds__(1024) void k_disp_rank_scan(const int32_t* __restri
   }
 }
 
+// Exclusive scan of v over a 256-thread block.
+__device__ __forceinline__ int block_excl_scan_256(int v, int* s_wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wsum[w];
+  __syncthreads();
+  return base + incl - v;
+}
+
+// The rank kernel of a dispatch issued beside an FFN launch on the other
+// stream.  A CU running the gate/up GEMM holds two of its workgroups, which
+// leave 64 VGPRs per SIMD lane and about 15 KB of LDS: a workgroup of
+// k_disp_rank_scan (1024 threads, 92 VGPRs, 19 KB) only starts once a CU has
+// drained.  This variant has 256 threads, at most 64 VGPRs and 6 KB of LDS, so
+// it fits beside the GEMM.  Same blocks of 1024 pairs, same results: the
+// block's pairs are ranked in four rounds of 256 in pair order, each round on
+// top of the running per-expert position the rounds before it left.
+constexpr int kLeanThreads = 256;
+
+__global__ __launch_bounds__(kLeanThreads) __attribute__((amdgpu_num_vgpr(64))) void k_disp_rank_scan_lean(
+    const int32_t* __restrict__ ids, int64_t n_pairs, int e_begin, int E_loc, int64_t nb, int parts, int tile_m,
+    const int32_t* __restrict__ block_hist, const int32_t* __restrict__ block_err, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_offsets, int32_t* __restrict__ err,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int s_pre[kMidMaxELoc];       // pairs of expert e in blocks before this one
+  __shared__ int s_run[kMidMaxELoc];       // pairs of expert e in all blocks, then the running position
+  __shared__ int s_wcnt[4][kMidMaxELoc];   // this round's count per wave and expert
+  __shared__ int s_wsum[4];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int64_t b = blockIdx.x;
+  for (int e = tid; e < E_loc; e += kLeanThreads) {
+    s_pre[e] = 0;
+    s_run[e] = 0;
+  }
+  __syncthreads();
+  if (tid < parts * E_loc) {
+    const int e = tid % E_loc;
+    const int part = tid / E_loc;
+    const int64_t per = (nb + parts - 1) / parts;
+    const int64_t r0 = min(nb, part * per);
+    const int64_t r1 = min(nb, r0 + per);
+    constexpr int U = 8;
+    int pre = 0, tot = 0;
+    for (int64_t r = r0; r < r1; r += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = r + u < r1 ? block_hist[(r + u) * E_loc + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        tot += v[u];
+        pre += r + u < b ? v[u] : 0;
+      }
+    }
+    if (pre) atomicAdd(&s_pre[e], pre);
+    if (tot) atomicAdd(&s_run[e], tot);
+  }
+  int any = 0;
+  if (b == 0)
+    for (int64_t q = tid; q < nb; q += kLeanThreads) any |= block_err[q];
+  any = __syncthreads_or(any);
+  const int cnt = tid < E_loc ? s_run[tid] : 0;
+  const int off = block_excl_scan_256(cnt, s_wsum);
+  if (b == 0) {
+    if (tid < E_loc) {
+      counts[tid] = cnt;
+      offsets[tid] = off;
+    }
+    if (tid == E_loc - 1) offsets[E_loc] = off + cnt;
+    if (tid == 0) err[0] = any;
+  }
+  if (tile_offsets) {
+    const int tiles = (cnt + tile_m - 1) / tile_m;
+    const int toff = block_excl_scan_256(tiles, s_wsum);
+    if (b == 0) {
+      if (tid < E_loc) tile_offsets[tid] = toff;
+      if (tid == E_loc - 1) tile_offsets[E_loc] = toff + tiles;
+    }
+  }
+  // every read of the totals is behind the scan's closing barrier
+  if (tid < E_loc) s_run[tid] = off + s_pre[tid];
+  for (int round = 0; round < kMidPairsPerBlock / kLeanThreads; ++round) {
+    const int64_t p0 = b * kMidPairsPerBlock + round * kLeanThreads;
+    if (p0 >= n_pairs) break;
+    for (int i = tid; i < 4 * E_loc; i += kLeanThreads) s_wcnt[i / E_loc][i % E_loc] = 0;
+    __syncthreads();
+    const int64_t p = p0 + tid;
+    int le = -1;
+    if (p < n_pairs) {
+      const int e = ids[p] - e_begin;
+      if (e >= 0 && e < E_loc) le = e;
+    }
+    const bool local = le >= 0;
+    uint64_t remaining = __ballot(local);
+    uint64_t mine = 0;
+    while (remaining) {
+      const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+      const int lead_e = __shfl(le, leader, kWave);
+      const uint64_t m = __ballot(local && le == lead_e);
+      if (local && le == lead_e) mine = m;
+      remaining &= ~m;
+    }
+    const uint64_t lower = mine & lanemask_lt();
+    if (local && lower == 0) s_wcnt[wave][le] = __popcll(mine);
+    __syncthreads();
+    if (p < n_pairs) {
+      int pos = -1;
+      if (local) {
+        pos = s_run[le] + __popcll(lower);
+        for (int w = 0; w < wave; ++w) pos += s_wcnt[w][le];
+        perm[pos] = static_cast<int32_t>(p);
+      }
+      inv[p] = pos;
+    }
+    __syncthreads();
+    if (tid < E_loc) s_run[tid] += s_wcnt[0][tid] + s_wcnt[1][tid] + s_wcnt[2][tid] + s_wcnt[3][tid];
+    __syncthreads();
+  }
+}
+
 // Small batches (few pairs, E_loc <= 256): count, scan and rank in one
 // workgroup, so the dispatch is two launches (this and the gather) instead of
 // four.  Pairs are taken 1024 at a time in order; inside a chunk a pair's
@@ -540,10 +663,18 @@ moe_status launch_dispatch_send(const DispatchArgs& a, hipStream_t s) {
                        dim3(kMidPairsPerBlock), 0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist,
                        w.block_err);
     DBOMOE_CHECK_LAUNCH();
-    const int parts = static_cast<int>(std::min<int64_t>(std::max(1, 1024 / E_loc), nb_mid));
-    hipLaunchKernelGGL(k_disp_rank_scan, dim3(static_cast<unsigned>(nb_mid)), dim3(1024), 0, s, a.ids, n_pairs,
-                       a.e_begin, E_loc, nb_mid, parts, a.tile_m > 0 ? a.tile_m : 1, w.block_hist, w.block_err,
-                       a.counts, a.offsets, a.tile_m > 0 ? a.tile_offsets : nullptr, w.err, a.perm, a.inv);
+    const int nt = a.beside_ffn ? kLeanThreads : 1024;
+    const int parts = static_cast<int>(std::min<int64_t>(std::max(1, nt / E_loc), nb_mid));
+    if (a.beside_ffn)
+      hipLaunchKernelGGL(k_disp_rank_scan_lean, dim3(static_cast<unsigned>(nb_mid)), dim3(kLeanThreads), 0, s,
+                         a.ids, n_pairs, a.e_begin, E_loc, nb_mid, parts, a.tile_m > 0 ? a.tile_m : 1,
+                         w.block_hist, w.block_err, a.counts, a.offsets, a.tile_m > 0 ? a.tile_offsets : nullptr,
+                         w.err, a.perm, a.inv);
+    else
+      hipLaunchKernelGGL(k_disp_rank_scan, dim3(static_cast<unsigned>(nb_mid)), dim3(1024), 0, s, a.ids,
+                         n_pairs, a.e_begin, E_loc, nb_mid, parts, a.tile_m > 0 ? a.tile_m : 1, w.block_hist,
+                         w.block_err, a.counts, a.offsets, a.tile_m > 0 ? a.tile_offsets : nullptr, w.err,
+                         a.perm, a.inv);
     DBOMOE_CHECK_LAUNCH();
     return MOE_OK;
   }

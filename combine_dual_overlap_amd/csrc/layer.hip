@@ -131,6 +131,7 @@ struct HipBackend {
   int64_t row0[2];
   int64_t rows[2];
   int n_mb;
+  int schedule;   // the schedule run (after the split rule)
 
   template <class T>
   T* buf(int mb, Buf b) const {
@@ -144,6 +145,16 @@ struct HipBackend {
     const char* xm = x + row0[mb] * d->H * as;
     const int k = d->route.k;
     const int E_loc = d->expert_end - d->expert_begin;
+    // The comm-stream stages that can run beside the other microbatch's FFN
+    // launch take the kernels that fit beside the GEMM: the second
+    // microbatch's dispatch, and the first one's combine unless the FFN event
+    // it waits for is the late one (recorded after the second FFN is queued,
+    // so nothing runs beside it).
+    const bool dispatch_stage =
+        stage == sched::kDispatch || stage == sched::kDispatchSend || stage == sched::kDispatchRecv;
+    const bool beside_ffn = stream == sched::kComm && n_mb == 2 &&
+                            ((dispatch_stage && mb == 1) ||
+                             (stage == sched::kCombine && mb == 0 && schedule != DBO_SCHED_DBO_LATE_EVENT));
     moe_status st = MOE_OK;
     switch (stage) {
       case sched::kRoute: {
@@ -160,7 +171,7 @@ struct HipBackend {
                        d->expert_end, 0, buf<int32_t>(mb, B_COUNTS), buf<int32_t>(mb, B_OFFSETS),
                        nullptr, buf<int32_t>(mb, B_PERM), buf<int32_t>(mb, B_INV),
                        buf<void>(mb, B_XPERM), buf<void>(mb, B_DISPWS), o->comm_cu_budget,
-                       d->fp8_act ? buf<uint8_t>(mb, B_XSCALE) : nullptr};
+                       d->fp8_act ? buf<uint8_t>(mb, B_XSCALE) : nullptr, beside_ffn};
         // timing: from the first dispatch kernel to the last (send start .. recv end)
         if (stage != sched::kDispatchRecv && ctx->timing &&
             hipEventRecord(ctx->tev[ctx->slot][mb][3], s) != hipSuccess)
@@ -216,7 +227,8 @@ struct HipBackend {
       case sched::kCombine: {
         CombineArgs a{buf<void>(mb, B_YPERM), d->act, T, d->H, k, buf<int32_t>(mb, B_INV), buf<float>(mb, B_W),
                       d->shared_I > 0 ? buf<void>(mb, B_SHOUT) : nullptr, out + row0[mb] * d->H * as,
-                      o->comm_cu_budget, d->shared_I > 0 ? dense_down_chunks(d->act, d->shared_I, d->I) : 0};
+                      o->comm_cu_budget, d->shared_I > 0 ? dense_down_chunks(d->act, d->shared_I, d->I) : 0,
+                      beside_ffn};
         if (ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][5], s) != hipSuccess) return MOE_ERR_HIP;
         st = launch_combine(a, s);
         if (st == MOE_OK && ctx->timing && hipEventRecord(ctx->tev[ctx->slot][mb][6], s) != hipSuccess)
@@ -396,6 +408,7 @@ extern "C" moe_status dbo_moe_layer(dbo_ctx* ctx, const moe_layer_desc* d, const
   be.out = static_cast<char*>(out);
   be.forced = forced_ids;
   be.bias = logit_bias;
+  be.schedule = schedule;
   if (schedule == DBO_SCHED_UNSPLIT) {
     be.row0[0] = 0;
     be.rows[0] = T;

@@ -75,6 +75,41 @@ def test_dbo_equals_serial_bitwise_and_repeatable(cid):
                            base.view(torch.int16) if base.dtype == torch.bfloat16 else base), sched
 
 
+@pytest.mark.parametrize("cid,small,fp8_act", [(3, True, False), (3, False, False), (4, False, False),
+                                                (5, False, False), (3, False, True)])
+def test_dispatch_and_combine_beside_ffn(cid, small, fp8_act):
+    """In the two-stream schedules the second microbatch's dispatch and the
+    first one's combine take the kernels sized to fit beside the GEMM (the
+    256-thread rank kernel over blocks of 1024 pairs, the 64-VGPR combine).
+    The second microbatch's counts, offsets, perm and inv equal the oracle's
+    dispatch of its ids bit for bit (ragged last block at the skewed shape),
+    its bf16 rows are the token rows they name, and the layer output equals
+    SERIAL's (the standard kernels) bitwise."""
+    inp, _ = inputs(cid, small)
+    cfg = inp["cfg"]
+    L = _layer(inp, fp8_act=fp8_act)
+    print(f"beside-ffn cfg={cfg.name} fp8_act={fp8_act}", flush=True)
+    base = L.run("serial").clone()
+    T0 = (cfg.T + 1) // 2
+    n1 = cfg.T - T0
+    for sched in ["dbo", "dbo_recv_hook", "dbo_late_event"]:
+        out = L.run(sched)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), base.view(torch.int16)), sched
+        ids = L.view(1, "topk_ids", torch.int32, (n1, cfg.k)).cpu().numpy()
+        ref = O.dispatch_ref(ids, cfg.expert_begin, cfg.expert_end)
+        M = int(ref["M"])
+        E_loc = cfg.E_loc
+        assert np.array_equal(L.view(1, "counts", torch.int32, (E_loc,)).cpu().numpy(), ref["counts"]), sched
+        assert np.array_equal(L.view(1, "offsets", torch.int32, (E_loc + 1,)).cpu().numpy(), ref["offsets"]), sched
+        assert np.array_equal(L.view(1, "perm", torch.int32, (M,)).cpu().numpy(), ref["perm"]), sched
+        assert np.array_equal(L.view(1, "inv", torch.int32, (n1 * cfg.k,)).cpu().numpy(), ref["inv"]), sched
+        if not fp8_act:
+            rows = inp["x"][T0 + torch.from_numpy(ref["perm"] // cfg.k).long()]
+            xp = L.view(1, "x_perm", torch.bfloat16, (M, cfg.H)).cpu()
+            assert torch.equal(xp.view(torch.int16), rows.view(torch.int16)), sched
+
+
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
 def test_layer_full_size_sampled(cid):
     inp, ov = inputs(cid, False)
