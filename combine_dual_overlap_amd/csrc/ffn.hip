@@ -18,13 +18,16 @@ namespace dbomoe {
 // Rows per expert under roughly uniform routing are about Poisson(mean): size
 // the row tile for the likely largest expert, so most experts take one row
 // tile (their weights stream once) and large experts get the big MFMA tile.
-// Measured on the five layer shapes (DBO schedule): 32-row tiles for decode,
-// 64 up to about 96 rows, 128 beyond.
+// An expert a row or two past a tile boundary streams its weights once more
+// for a nearly empty tile, which costs more than the idle MFMA rows of the
+// larger tile: at 64 +- 8 rows per expert (the R1-shaped share) 128-row tiles
+// against 64 took the DBO layer from 0.969 to 0.933 ms (gate/up 286 -> 267 us,
+// down 144 -> 137 us).
 static int choose_tile_m(int64_t mean_rows) {
   const double m = static_cast<double>(mean_rows);
   const double est_max = m + 3.0 * std::sqrt(m) + 1.0;
   if (est_max <= 32) return 32;
-  if (est_max <= 96) return 64;
+  if (est_max <= 64) return 64;
   return 128;
 }
 

@@ -75,8 +75,10 @@ def test_ffn_auto_tile_choice():
     # decode-sized experts (Poisson(12) rows: the largest fits 32)
     assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_BF16, 2048, 1408, 12, 128, 2816) == 32
     assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 7168, 2048, 12) == 32
-    # about 64 rows per expert
-    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 7168, 2048, 64) == 64
+    # about 36 rows per expert (the largest fits 64); about 64 (the largest
+    # does not: one 128-row tile each rather than a second, nearly empty one)
+    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 7168, 2048, 36) == 64
+    assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 7168, 2048, 64) == 128
     # prefill-sized experts
     assert B.moe_ffn_auto_tile(B.MOE_BF16, B.MOE_FP8_E4M3FN, 2048, 768, 256) == 128
     assert B.moe_ffn_auto_tile(B.MOE_F32, B.MOE_F32, 128, 256, 8) == 32
