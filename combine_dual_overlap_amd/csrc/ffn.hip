@@ -47,7 +47,7 @@ static bool k_multiple_of(const GemmParams& g, int bk) {
 }
 
 template <int MODE, bool FP8>
-static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g) {
+static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g, bool full_tiles = false) {
   // bf16 weights, 128-row tiles: activation and weight tiles staged by LDS
   // DMA (bitwise equal to the register-staged kernel; measured
   // standalone on the skewed-layer shapes: gate/up 401 -> 367 us, down 217 ->
@@ -67,13 +67,27 @@ static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g) {
   // stays faster for gate/up (308.2 against 329.7 us standalone) and for the
   // 64-row down tiles of the R1-shaped share in the layer (148.5 against
   // 166.7 us, although 141.5 against 154.5 us standalone).
+  // With full_tiles (about 128 rows per expert or more: full 128-row tiles,
+  // MFMA-bound) the tiles keep one accumulator (ONE_ACC) and a two-stage ring,
+  // three 2 x 2 workgroups per CU: Qwen3-shaped prefill layer (DBO) 1.015 ->
+  // 0.957 ms, gate/up 287 -> 266 us, down 165 -> 157 us.  On the R1-shaped
+  // share (64 rows per expert, weight streaming) the two-stage ring lost
+  // (gate/up 258 -> 285 us), so it keeps the block accumulator and three
+  // stages.  Tiles of 64 and 128 rows of one launch take the same arithmetic,
+  // so the row tile does not change the result.
   if (FP8 && (bm == 64 || bm == 128) && g.rows1 == 0 && g.g[0].K / 128 <= kW8MaxKBlocks) {
-    if (MODE == MODE_DOWN && bm == 128)
+    if (full_tiles) {
+      if (bm == 128)
+        hipLaunchKernelGGL((k_gemm_fp8w<MODE, 128, 2, 2, 2, true>), grid, dim3(256), 0, s, g);
+      else
+        hipLaunchKernelGGL((k_gemm_fp8w<MODE, 64, 2, 2, 3, true>), grid, dim3(256), 0, s, g);
+    } else if (MODE == MODE_DOWN && bm == 128) {
       hipLaunchKernelGGL((k_gemm_fp8w<MODE, 128, 2, 4>), grid, dim3(512), 0, s, g);
-    else if (bm == 128)
+    } else if (bm == 128) {
       hipLaunchKernelGGL((k_gemm_fp8w<MODE, 128>), grid, dim3(256), 0, s, g);
-    else
+    } else {
       hipLaunchKernelGGL((k_gemm_fp8w<MODE, 64>), grid, dim3(256), 0, s, g);
+    }
     return;
   }
   if (bm == 32 && k_multiple_of(g, 2 * kBK))
@@ -327,15 +341,16 @@ moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   }
   const bool fp8_launch = fp8 && a.cap_rows > 0;
 
+  const bool full_tiles = a.rows_hint >= 128;
   if (a.t0 && hipEventRecord(a.t0, s) != hipSuccess) return MOE_ERR_HIP;
   if (fp8_launch)
-    launch_mfma<MODE_GATEUP, true>(bm, grid1, s, p1);
+    launch_mfma<MODE_GATEUP, true>(bm, grid1, s, p1, full_tiles);
   else
     launch_mfma<MODE_GATEUP, false>(bm, grid1, s, p1);
   DBOMOE_CHECK_LAUNCH();
   if (a.t1 && hipEventRecord(a.t1, s) != hipSuccess) return MOE_ERR_HIP;
   if (fp8_launch)
-    launch_mfma<MODE_DOWN, true>(bm, grid2, s, p2);
+    launch_mfma<MODE_DOWN, true>(bm, grid2, s, p2, full_tiles);
   else
     launch_mfma<MODE_DOWN, false>(bm, grid2, s, p2);
   DBOMOE_CHECK_LAUNCH();

@@ -9,11 +9,22 @@
 // third run), and no register ring or LDS store sits on the load path.
 //
 // The weights stay fp8 in LDS.  Each wave converts its fragments exactly to
-// bf16 when it reads them (every e4m3 value is a bf16 value) and the MFMAs sum
-// code value x activation over one 128-wide K block into a block accumulator;
-// at the end of the block the fp32 accumulator takes s x block (one fma), s
-// being the block's scale.  This is the block-scaled product as defined, with
-// no rounding of the weights: code value x s is never formed.
+// bf16 when it reads them (every e4m3 value is a bf16 value), so the MFMAs
+// sum code value x activation over each 128-wide K block; code value x s is
+// never formed or rounded.  The block scale s is applied in one of two ways:
+//  * block accumulator: the block's MFMAs sum into a block accumulator, and at
+//    the end of the block the fp32 accumulator takes s x block (one fma);
+//  * one accumulator (ONE_ACC): the accumulator is kept in units of the
+//    current K block's scale: entering block b it is multiplied by
+//    s_prev / s_b, the block's MFMAs add into it directly, and the last
+//    block's scale is applied at the end.  Mathematically the same sum, with
+//    one fp32 rounding per block boundary (relative 2^-24 each); it needs
+//    the partial sums divided by a block scale to stay within the fp32 range.
+//    A block whose scale is zero contributes nothing: the weight codes of the
+//    columns it scales are masked to zero for that block (every code read is
+//    ANDed with its scale row's mask, no branch).  Half the accumulator registers (156 against
+//    224 VGPRs at 128 rows), which with a two-stage ring (49 KB of LDS) lets
+//    three workgroups share a CU instead of two.
 //
 // K order: within a 64-wide stage, lane group q = lane / 16 of an MFMA
 // supplies K offsets 16q + 8kk .. 16q + 8kk + 7 for the stage's MFMA step kk
@@ -64,7 +75,7 @@ template <int BM, int NBUF> struct W8Lds {
   static constexpr int bytes = NBUF * (A + B) + S;
 };
 
-template <int MODE, int BM, int WAVES_M, int WAVES_N, int NBUF>
+template <int MODE, int BM, int WAVES_M, int WAVES_N, int NBUF, bool ONE_ACC>
 __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
                                                uint8_t* lds) {
   constexpr int BN = kBN, BK = kBK, NW = WAVES_M * WAVES_N;
@@ -75,7 +86,7 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   constexpr int NQB = BN / 16 / NW;          // weight DMAs per wave per stage (16 rows each)
   constexpr int NDMA = NQA + NQB;
   static_assert(NQA >= 1 && NQB >= 1 && NQA * NW * 8 == BM && NQB * NW * 16 == BN, "DMA split");
-  static_assert(NBUF >= 3 && (NBUF - 2) * NDMA < 64, "ring depth");
+  static_assert(NBUF >= 2 && (NBUF - 2) * NDMA < 64, "ring depth");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int K = g.K, KT = K / BK, nt = t.nt;
@@ -140,7 +151,7 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
     for (int i = 0; i < NQB; ++i) lds_dma16(lds_b + buf * B_BYTES + (wave * NQB + i) * 1024, b_src[i] + k0);
   };
 
-  f32x4_t acc[TM][TN], blk[TM][TN];
+  f32x4_t acc[TM][TN], blk[TM][TN];   // blk: block accumulator (unused with ONE_ACC)
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -148,6 +159,11 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
       acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       blk[i][j] = acc[i][j];
     }
+  // ONE_ACC: per scale row (gate, up; a down tile uses the first), the scale
+  // the accumulator is expressed in and whether the current block's is nonzero
+  float unit[2] = {1.f, 1.f};
+  uint32_t code_mask[2] = {~0u, ~0u};
+  auto half = [](int tn) { return (MODE == MODE_GATEUP && tn >= TN / 2) ? 1 : 0; };
   const int frag_row = lane & 15, q = lane >> 4;
   const int tm_valid = __builtin_amdgcn_readfirstlane(
       max(0, min(TM, (t.rows - t.m_off - wm * WM + 15) / 16)));
@@ -155,6 +171,8 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) b_off[tn] = w8_off(b_lds_row<MODE, WN, TN, BN>(wn, tn) + frag_row, q);
 
+  using True = std::integral_constant<bool, true>;
+  using False = std::integral_constant<bool, false>;
   // MFMAs of one stage into the block accumulator (FIRST: the block's first
   // stage, whose first step starts from zero).
   auto compute = [&](int buf, auto first, auto full) {
@@ -165,8 +183,11 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
     const uint8_t* B = sB + buf * B_BYTES;
     bf16x8_t blo[TN], bhi[TN];
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-      fp8x16_to_bf16_exact(*reinterpret_cast<const u32x4_t*>(B + b_off[tn]), blo[tn], bhi[tn]);
+    for (int tn = 0; tn < TN; ++tn) {
+      u32x4_t c = *reinterpret_cast<const u32x4_t*>(B + b_off[tn]);
+      if constexpr (ONE_ACC) c &= code_mask[half(tn)];
+      fp8x16_to_bf16_exact(c, blo[tn], bhi[tn]);
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8_t af[TM];
@@ -179,10 +200,35 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
         if (decltype(full)::value || tm < tm_valid)
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn) {
-            const f32x4_t c = (decltype(first)::value && kk == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : blk[tm][tn];
-            blk[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], kk == 0 ? blo[tn] : bhi[tn], c, 0, 0, 0);
+            if constexpr (ONE_ACC) {
+              acc[tm][tn] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], kk == 0 ? blo[tn] : bhi[tn], acc[tm][tn], 0, 0, 0);
+            } else {
+              const f32x4_t c = (decltype(first)::value && kk == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : blk[tm][tn];
+              blk[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], kk == 0 ? blo[tn] : bhi[tn], c, 0, 0, 0);
+            }
           }
     }
+  };
+  // ONE_ACC, entering K block kb: the accumulator into units of its scale
+  auto enter_block = [&](int kb, auto full) {
+    if (!decltype(full)::value && tm_valid == 0) return;
+    float r[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float sb = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sS[h * kW8MaxKBlocks + kb])));
+      const bool live = sb != 0.f;
+      code_mask[h] = live ? ~0u : 0u;
+      r[h] = live ? unit[h] / sb : 1.f;
+      unit[h] = live ? sb : unit[h];
+    }
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+      if (decltype(full)::value || tm < tm_valid)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[tm][tn][e] *= r[half(tn)];
   };
   // acc += s * blk for K block kb
   auto scale_block = [&](int kb, auto full) {
@@ -212,13 +258,16 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   auto stage = [&](int kt, int buf, auto first, auto full) {
     const int ahead = kt + NBUF - 1;
     if (ahead < KT) issue(ahead, buf == 0 ? NBUF - 1 : buf - 1);
+    if constexpr (ONE_ACC) {
+      if (decltype(first)::value) enter_block(kt >> 1, full);
+    }
     compute(buf, first, full);
-    if (!decltype(first)::value) scale_block(kt >> 1, full);
+    if constexpr (!ONE_ACC) {
+      if (!decltype(first)::value) scale_block(kt >> 1, full);
+    }
     wait_stages<NDMA, NBUF - 2>(min(KT - 1, ahead) - (kt + 1));
     __syncthreads();
   };
-  using True = std::integral_constant<bool, true>;
-  using False = std::integral_constant<bool, false>;
   // KT is even (K is a multiple of 128): two stages per K block.
   auto run = [&](auto full) {
     int buf = 0;                               // kt % NBUF
@@ -233,6 +282,14 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
     run(True{});
   else
     run(False{});
+  if constexpr (ONE_ACC) {   // into real units: the last nonzero block scale
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[tm][tn][e] *= unit[half(tn)];
+  }
   store_tile<BM, WAVES_M, WAVES_N, MODE, BN>(g, t, p, acc, reinterpret_cast<bf16_t*>(sA));
 }
 
@@ -247,7 +304,7 @@ template <int BM, int NW, int NBUF> struct W8Occ {
 
 // Group 0 only (a launch without a dense group of shared experts); K a
 // multiple of 128 with at most kW8MaxKBlocks blocks.
-template <int MODE, int BM, int WAVES_M = 2, int WAVES_N = 2, int NBUF = 3>
+template <int MODE, int BM, int WAVES_M = 2, int WAVES_N = 2, int NBUF = 3, bool ONE_ACC = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, (W8Occ<BM, WAVES_M * WAVES_N, NBUF>::value))
 void k_gemm_fp8w(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[W8Lds<BM, NBUF>::bytes];
@@ -255,7 +312,7 @@ void k_gemm_fp8w(GemmParams p) {
   TileLoc t;
   if (!locate_tile<BM>(p, s_loc, t)) return;
   __syncthreads();                                  // s_loc read by all before the ring is filled
-  gemm_tile_fp8w<MODE, BM, WAVES_M, WAVES_N, NBUF>(p.g[0], t, p, lds);
+  gemm_tile_fp8w<MODE, BM, WAVES_M, WAVES_N, NBUF, ONE_ACC>(p.g[0], t, p, lds);
 }
 
 }  // namespace dbomoe

@@ -213,8 +213,16 @@ moe_status moe_get_device_error(const void* dispatch_ws, int32_t* code, void* st
  *            MOE_ERR_INVALID_ARG
  *   ws       moe_ffn_workspace_size(cap_rows, I, act) bytes (holds h)
  * H % 128 == 0 and I % 64 == 0 (fp8: I % 128 == 0), else MOE_ERR_UNSUPPORTED.
- * fp8 weights are expanded to bf16 (code value x block scale, rounded once) on
- * their way to the MFMA tiles.
+ * fp8 weights: the 64- and 128-row tiles of routed experts (no dense group,
+ * K <= 64 scale blocks) convert the codes exactly and apply each block scale
+ * to the fp32 sum over its 128-wide K block: with a block accumulator (one
+ * fma per block), or, when the launch has about 128 rows per expert or more,
+ * with one accumulator kept in units of the current block's scale (rescaled
+ * at each block, one fp32 rounding per block).  That form needs the partial
+ * sums divided by a block scale to stay within the fp32 range (nonzero scales
+ * of one 128-row block within about 2^80 of each other); zero scales are
+ * allowed and contribute nothing.  The 32-row tiles and launches with a dense
+ * group expand code value x scale to bf16 (rounded once) before the MFMAs.
  * ------------------------------------------------------------------------- */
 size_t moe_ffn_workspace_size(int64_t cap_rows, int32_t I, moe_dtype act);
 /* The row tile the automatic choice (tile_m = 0) takes for experts of about

@@ -321,12 +321,13 @@ def test_bf16_row_tiles_agree(cid):
 
 @pytest.mark.parametrize("cid", [3, 4])
 def test_fp8_weight_row_tiles_agree(cid):
-    """fp8 weights: the DMA-staged tiles of 64 and 128 rows (gate/up 2 x 2
-    waves; down 2 x 2 and 2 x 4 waves) add the same fp32 block sums, each
-    scaled by its block scale with one fma, in the same K order, so their
-    outputs are equal bit for bit.  (Each tile, and the register-staged
-    32-row tile that rounds the weights first, is checked against the oracle
-    by test_grouped_ffn.)"""
+    """fp8 weights: the DMA-staged tiles of 64 and 128 rows of one launch
+    (gate/up 2 x 2 waves; down 2 x 2 or 2 x 4 waves) take the same arithmetic
+    (block sums scaled with one fma each, or at prefill sizes one accumulator
+    rescaled at every block) in the same K order, so their outputs are equal
+    bit for bit.  (Each tile, and the register-staged 32-row tile that
+    rounds the weights first, is checked against the oracle by
+    test_grouped_ffn.)"""
     C = _gpu()
     inp, ov = inputs(cid, True)
     cfg = inp["cfg"]
@@ -341,30 +342,37 @@ def test_fp8_weight_row_tiles_agree(cid):
     assert torch.equal(y64.view(torch.int16), y128.view(torch.int16)), "64 vs 128 rows"
 
 
-def _fp8_experts(E, rows, cols, gen, zero_block_of=None):
+def _fp8_experts(E, rows, cols, gen, zero_block_of=None, spread=4.0, zero_scales=False):
     """E expert matrices of block-quantised fp8 weights: N(0, 0.02) scaled by
-    2^u, u ~ U(-4, 4), per 128 x 128 block (so block scales differ), and one
-    all-zero block in expert zero_block_of."""
+    2^u, u ~ U(-spread, spread), per 128 x 128 block (so block scales differ),
+    and one all-zero block in expert zero_block_of (the quantiser gives it
+    scale 1).  zero_scales: about one block in four gets scale 0 while its
+    codes stay as drawn (the block contributes nothing)."""
     codes = torch.empty(E, rows, cols, dtype=torch.uint8)
     scales = torch.empty(E, rows // 128, cols // 128, dtype=torch.float32)
     for e in range(E):
-        u = (torch.rand(rows // 128, cols // 128, generator=gen) * 8.0 - 4.0)
+        u = (torch.rand(rows // 128, cols // 128, generator=gen) * (2 * spread) - spread)
         f = torch.pow(2.0, u).repeat_interleave(128, 0).repeat_interleave(128, 1)
         w = torch.randn(rows, cols, generator=gen) * 0.02 * f
         if e == zero_block_of:
             w[:128, :128] = 0.0
         codes[e], scales[e] = W.quantize_fp8_blocks(w)
+        if zero_scales:
+            scales[e][torch.rand(rows // 128, cols // 128, generator=gen) < 0.25] = 0.0
     return codes, scales
 
 
-def _fp8_ffn_vs_oracle(C, H, I, counts, tiles, seed):
+def _fp8_ffn_vs_oracle(C, H, I, counts, tiles, seed, spread=4.0, zero_scales=False):
     gen = torch.Generator().manual_seed(seed)
     E = len(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     M = int(offsets[-1])
     x = torch.randn(M, H, generator=gen).to(torch.bfloat16)
-    c13, s13 = _fp8_experts(E, 2 * I, H, gen, zero_block_of=min(2, E - 1))
-    c2, s2 = _fp8_experts(E, H, I, gen)
+    c13, s13 = _fp8_experts(E, 2 * I, H, gen, zero_block_of=min(2, E - 1), spread=spread, zero_scales=zero_scales)
+    c2, s2 = _fp8_experts(E, H, I, gen, spread=spread, zero_scales=zero_scales)
+    if zero_scales:
+        assert (s13 == 0).any() and (s2 == 0).any() and (c13[s13.repeat_interleave(128, 1).repeat_interleave(
+            128, 2) == 0] != 0).any()
     want, scale = O.grouped_ffn_ref(
         O.decode(W.bits(x), "bf16"), offsets,
         lambda e: (O.dequant_fp8_blocks(c13[e].numpy(), s13[e].numpy()),
@@ -381,6 +389,16 @@ def test_fp8_weight_ffn_ragged_experts():
     257 rows: partial last row tiles, waves without rows, several row tiles;
     varied block scales and an all-zero weight block (scale 1)."""
     _fp8_ffn_vs_oracle(_gpu(), 256, 256, np.array([1, 0, 33, 64, 65, 128, 129, 257]), (32, 64, 128), 21)
+
+
+@pytest.mark.parametrize("counts", [[1, 0, 33, 64, 65, 128, 129, 257], [0, 1, 127, 128, 129, 200, 257, 300]])
+def test_fp8_weight_ffn_zero_and_wide_block_scales(counts):
+    """Block scales spread over 2^-20 .. 2^20 and about a quarter of them
+    zero (over nonzero codes), at about 85 rows per expert (block
+    accumulator, one fma per block) and about 140 (full tiles: one
+    accumulator kept in units of the current block's scale, zero-scale blocks
+    masked); row tiles of 64 and 128 and the automatic choice."""
+    _fp8_ffn_vs_oracle(_gpu(), 512, 256, np.array(counts), (0, 64, 128), 23, spread=20.0, zero_scales=True)
 
 
 def test_fp8_weight_ffn_k_beyond_dma_scale_rows():
