@@ -415,8 +415,8 @@ def trace_steps(L, run, schedules, n, torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200, help="timed graph-replayed DBO steps (200 steps of the prefill layer: about 0.2 s, long enough to average the few-percent drift of the chip's speed over sub-second windows)")
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="layer configuration 1..5 (default 3)")
     ap.add_argument("--rounds", type=int, default=10, help="interleaved trial rounds per schedule")
     ap.add_argument("--trial-steps", type=int, default=20, help="steps per trial")
