@@ -66,6 +66,22 @@ __device__ __forceinline__ void fp8x16_to_bf16_exact(const u32x4_t& c, bf16x8_t&
   hi = __builtin_bit_cast(bf16x8_t, u32x4_t{o[4], o[5], o[6], o[7]});
 }
 
+// Waits until at most n of this wave's DMAs are in flight, n counted at run
+// time (DMAs complete in issue order); n above MAXN waits for MAXN, which is
+// only stricter.
+template <int MAXN>
+__device__ __forceinline__ void wait_dmas(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN>();
+      return;
+    }
+    wait_dmas<MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // K blocks of one tile's scale rows (one 64-lane dword DMA per row)
 constexpr int kW8MaxKBlocks = 64;
 template <int BM, int NBUF> struct W8Lds {
@@ -100,6 +116,13 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   // Activation DMA i of this wave fills tile rows 8 (wave NQA + i) .. + 7:
   // lane l takes row l / 8 of the group and its 16-byte chunk (l % 8) ^ (l / 8),
   // the XOR-swizzled order of lds_off_k (rows past the expert: its last row).
+  // Only the first na of them carry a row of the tile; the others are not
+  // issued, and the LDS rows they would fill feed only output rows that are
+  // never stored (an output row depends on its own activation row alone).  So
+  // a wave issues nd = na + NQB DMAs per stage, a count fixed for the tile.
+  const int na = __builtin_amdgcn_readfirstlane(
+      max(0, min(NQA, (t.rows - t.m_off - 8 * wave * NQA + 7) / 8)));
+  const int nd = na + NQB;
   const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
   const bf16_t* a_src[NQA];
 #pragma unroll
@@ -146,7 +169,8 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   auto issue = [&](int kt, int buf) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < NQA; ++i) lds_dma16(lds_a + buf * A_BYTES + (wave * NQA + i) * 1024, a_src[i] + k0);
+    for (int i = 0; i < NQA; ++i)
+      if (i < na) lds_dma16(lds_a + buf * A_BYTES + (wave * NQA + i) * 1024, a_src[i] + k0);
 #pragma unroll
     for (int i = 0; i < NQB; ++i) lds_dma16(lds_b + buf * B_BYTES + (wave * NQB + i) * 1024, b_src[i] + k0);
   };
@@ -248,12 +272,12 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   // Ring of NBUF stages: stage kt lives in buffer kt % NBUF.  Stage kt issues
   // the DMAs of stage kt + NBUF - 1 into the buffer stage kt - 1 used (every
   // wave left it at the previous barrier), runs its MFMAs, waits for its own
-  // DMAs of stage kt + 1 (later stages may stay in flight) and meets the
+  // nd DMAs of stage kt + 1 (later stages may stay in flight) and meets the
   // other waves at the barrier.  The wait before the first stage also covers
   // wave 0's scale DMAs, which were issued before any stage.
   const int pre = min(NBUF - 1, KT);
   for (int s = 0; s < pre; ++s) issue(s, s);
-  wait_stages<NDMA, NBUF - 2>(pre - 1);
+  wait_dmas<(NBUF - 2) * NDMA>((pre - 1) * nd);
   __syncthreads();
   auto stage = [&](int kt, int buf, auto first, auto full) {
     const int ahead = kt + NBUF - 1;
@@ -265,7 +289,7 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
     if constexpr (!ONE_ACC) {
       if (!decltype(first)::value) scale_block(kt >> 1, full);
     }
-    wait_stages<NDMA, NBUF - 2>(min(KT - 1, ahead) - (kt + 1));
+    wait_dmas<(NBUF - 2) * NDMA>((min(KT - 1, ahead) - (kt + 1)) * nd);
     __syncthreads();
   };
   // KT is even (K is a multiple of 128): two stages per K block.
