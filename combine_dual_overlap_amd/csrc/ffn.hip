@@ -51,9 +51,14 @@ static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g, b
   // bf16 weights, 128-row tiles: activation and weight tiles staged by LDS
   // DMA (bitwise equal to the register-staged kernel; measured
   // standalone on the skewed-layer shapes: gate/up 401 -> 367 us, down 217 ->
-  // 197 us).
+  // 197 us).  The down GEMM runs 8 waves per tile, 2 x 4 at 4 per SIMD: the
+  // skewed layer (DBO) 1.096 -> 1.078 ms, down 180 -> 169 us; 2 x 4 gate/up
+  // tiles gained nothing there (330 -> 333 us).
   if (!FP8 && bm == 128 && k_multiple_of(g, kBK)) {
-    hipLaunchKernelGGL((k_gemm_dma<MODE>), grid, dim3(256), 0, s, g);
+    if (MODE == MODE_DOWN)
+      hipLaunchKernelGGL((k_gemm_dma<MODE, 128, kBN, kBK, 2, false, 4, 4>), grid, dim3(512), 0, s, g);
+    else
+      hipLaunchKernelGGL((k_gemm_dma<MODE>), grid, dim3(256), 0, s, g);
     return;
   }
   // fp8 weights, 64- or 128-row tiles, no dense group: fp8 codes staged by LDS

@@ -633,19 +633,19 @@ template <int BM, int BN, int BK, int NBUF> struct DmaLds {
   static constexpr int A = BM * BK * 2, B = BN * BK * 2, bytes = NBUF * (A + B);
 };
 
-template <int MODE, int BM, int BN, int BK, int NBUF, bool ROT>
+template <int MODE, int BM, int BN, int BK, int NBUF, bool ROT, int WAVES_N = 2>
 __device__ __forceinline__ void gemm_tile_dma(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
                                               uint8_t* lds) {
-  constexpr int WAVES_M = 2, WAVES_N = 2;
+  constexpr int WAVES_M = 2, NW = WAVES_M * WAVES_N;
   using S = TileShape<BM, WAVES_M, WAVES_N, BN>;
   constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
-  constexpr int CPR = BK / 8, RPD = 64 / CPR;            // chunks per row, rows per DMA
-  constexpr int NQA = BM / RPD / 4, NQB = BN / RPD / 4;  // DMAs per wave per stage
+  constexpr int CPR = BK / 8, RPD = 64 / CPR;              // chunks per row, rows per DMA
+  constexpr int NQA = BM / RPD / NW, NQB = BN / RPD / NW;  // DMAs per wave per stage
   constexpr int NDMA = NQA + NQB;
   constexpr int A_BYTES = DmaLds<BM, BN, BK, NBUF>::A, B_BYTES = DmaLds<BM, BN, BK, NBUF>::B;
-  static_assert(NQA >= 1 && NQB >= 1 && NQA * 4 * RPD == BM && NQB * 4 * RPD == BN, "DMA split");
+  static_assert(NQA >= 1 && NQB >= 1 && NQA * NW * RPD == BM && NQB * NW * RPD == BN, "DMA split");
   static_assert(NBUF >= 2 && (NBUF - 2) * NDMA < 64, "ring");
-  static_assert(4 * WM * (MODE == MODE_GATEUP ? WN / 2 : WN) * 2 <= NBUF * A_BYTES, "epilogue scratch");
+  static_assert(NW * WM * (MODE == MODE_GATEUP ? WN / 2 : WN) * 2 <= NBUF * A_BYTES, "epilogue scratch");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int K = g.K, KT = K / BK, nt = t.nt;
@@ -760,15 +760,16 @@ __global__ __launch_bounds__(256, (MinWaves<BM, BK>::value)) void k_gemm_nt(Gemm
 }
 
 // bf16 tiles with DMA staging; both groups (a dense group of shared experts
-// runs through the same tile).
-template <int MODE, int BM = 128, int BN = kBN, int BK = kBK, int NBUF = 2, bool ROT = false, int MINW = 2>
-__global__ __launch_bounds__(256, MINW) void k_gemm_dma(GemmParams p) {
+// runs through the same tile).  2 x WAVES_N waves (MINW: waves per SIMD).
+template <int MODE, int BM = 128, int BN = kBN, int BK = kBK, int NBUF = 2, bool ROT = false, int MINW = 2,
+          int WAVES_N = 2>
+__global__ __launch_bounds__(2 * WAVES_N * 64, MINW) void k_gemm_dma(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[DmaLds<BM, BN, BK, NBUF>::bytes];
   int* s_loc = reinterpret_cast<int*>(lds);
   TileLoc t;
   if (!locate_tile<BM>(p, s_loc, t)) return;
   __syncthreads();                                  // s_loc read by all before the ring is filled
-  gemm_tile_dma<MODE, BM, BN, BK, NBUF, ROT>(p.g[t.grp], t, p, lds);
+  gemm_tile_dma<MODE, BM, BN, BK, NBUF, ROT, WAVES_N>(p.g[t.grp], t, p, lds);
 }
 
 // Worst-case number of row tiles: sum_e ceil(n_e / BM) <= ceil(cap / BM) + E_loc.
