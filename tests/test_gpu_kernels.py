@@ -322,10 +322,10 @@ def test_bf16_row_tiles_agree(cid):
 @pytest.mark.parametrize("cid", [3, 4])
 def test_fp8_weight_row_tiles_agree(cid):
     """fp8 weights: the DMA-staged tiles of 64 and 128 rows of one launch
-    (gate/up 2 x 2 waves; down 2 x 2 or 2 x 4 waves) take the same arithmetic
-    (block sums scaled with one fma each, or at prefill sizes one accumulator
-    rescaled at every block) in the same K order, so their outputs are equal
-    bit for bit.  (Each tile, and the register-staged 32-row tile that
+    (gate/up 2 x 2 waves; down 2 x 2 or 2 x 4 waves) and the automatic choice
+    take the same arithmetic (block sums scaled with one fma each, or at
+    prefill sizes one accumulator rescaled at every block) in the same K
+    order, so their outputs are equal bit for bit.  (Each tile, and the register-staged 32-row tile that
     rounds the weights first, is checked against the oracle by
     test_grouped_ffn.)"""
     C = _gpu()
@@ -337,9 +337,10 @@ def test_fp8_weight_row_tiles_agree(cid):
     off = torch.from_numpy(ref["offsets"]).cuda()
     args = (cfg.I, off, cfg.E_loc, inp["w13"].cuda(), inp["w2"].cuda(), inp["w13_scale"].cuda(),
             inp["w2_scale"].cuda())
-    y64, y128 = (_ffn(C, x_perm, *args, tile_m=tm)[:ref["M"]] for tm in (64, 128))
+    y0, y64, y128 = (_ffn(C, x_perm, *args, tile_m=tm)[:ref["M"]] for tm in (0, 64, 128))
     assert torch.isfinite(y64.float()).all()
     assert torch.equal(y64.view(torch.int16), y128.view(torch.int16)), "64 vs 128 rows"
+    assert torch.equal(y0.view(torch.int16), y128.view(torch.int16)), "automatic vs 128 rows"
 
 
 def _fp8_experts(E, rows, cols, gen, zero_block_of=None, spread=4.0, zero_scales=False):
