@@ -22,7 +22,8 @@
 //    the partial sums divided by a block scale to stay within the fp32 range.
 //    A block whose scale is zero contributes nothing: the weight codes of the
 //    columns it scales are masked to zero for that block (every code read is
-//    ANDed with its scale row's mask, no branch).  Half the accumulator registers (156 against
+//    ANDed with its scale row's mask, no branch; a tile without a zero scale
+//    runs a copy of the loop without the mask).  Half the accumulator registers (156 against
 //    224 VGPRs at 128 rows), which with a two-stage ring (49 KB of LDS) lets
 //    three workgroups share a CU instead of two.
 //
@@ -199,7 +200,7 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   using False = std::integral_constant<bool, false>;
   // MFMAs of one stage into the block accumulator (FIRST: the block's first
   // stage, whose first step starts from zero).
-  auto compute = [&](int buf, auto first, auto full) {
+  auto compute = [&](int buf, auto first, auto full, auto mask) {
     // a wave with no rows in this tile (the last row tile of an expert) only
     // stages its share of the DMAs and meets the barriers
     if (!decltype(full)::value && tm_valid == 0) return;
@@ -209,7 +210,7 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       u32x4_t c = *reinterpret_cast<const u32x4_t*>(B + b_off[tn]);
-      if constexpr (ONE_ACC) c &= code_mask[half(tn)];
+      if constexpr (ONE_ACC && decltype(mask)::value) c &= code_mask[half(tn)];
       fp8x16_to_bf16_exact(c, blo[tn], bhi[tn]);
     }
 #pragma unroll
@@ -279,13 +280,13 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   for (int s = 0; s < pre; ++s) issue(s, s);
   wait_dmas<(NBUF - 2) * NDMA>((pre - 1) * nd);
   __syncthreads();
-  auto stage = [&](int kt, int buf, auto first, auto full) {
+  auto stage = [&](int kt, int buf, auto first, auto full, auto mask) {
     const int ahead = kt + NBUF - 1;
     if (ahead < KT) issue(ahead, buf == 0 ? NBUF - 1 : buf - 1);
     if constexpr (ONE_ACC) {
       if (decltype(first)::value) enter_block(kt >> 1, full);
     }
-    compute(buf, first, full);
+    compute(buf, first, full, mask);
     if constexpr (!ONE_ACC) {
       if (!decltype(first)::value) scale_block(kt >> 1, full);
     }
@@ -293,19 +294,34 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
     __syncthreads();
   };
   // KT is even (K is a multiple of 128): two stages per K block.
-  auto run = [&](auto full) {
+  auto run = [&](auto full, auto mask) {
     int buf = 0;                               // kt % NBUF
     for (int kt = 0; kt < KT; kt += 2) {
       const int b1 = buf == NBUF - 1 ? 0 : buf + 1;
-      stage(kt, buf, True{}, full);
-      stage(kt + 1, b1, False{}, full);
+      stage(kt, buf, True{}, full, mask);
+      stage(kt + 1, b1, False{}, full, mask);
       buf = b1 == NBUF - 1 ? 0 : b1 + 1;
     }
   };
-  if (tm_valid == TM)
-    run(True{});
-  else
-    run(False{});
+  // ONE_ACC: only a tile whose scale rows hold a zero runs the loop that masks
+  // the codes (the mask costs ~3 % of the gate/up GEMM); the scale rows are in
+  // LDS since the wait and barrier above.
+  bool any_zero = false;
+  if constexpr (ONE_ACC) {
+    const bool z = lane < kblocks && (sS[lane] == 0.f || sS[kW8MaxKBlocks + lane] == 0.f);
+    any_zero = __ballot(z) != 0;
+  }
+  if (tm_valid == TM) {
+    if (any_zero)
+      run(True{}, True{});
+    else
+      run(True{}, False{});
+  } else {
+    if (any_zero)
+      run(False{}, True{});
+    else
+      run(False{}, False{});
+  }
   if constexpr (ONE_ACC) {   // into real units: the last nonzero block scale
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
