@@ -348,7 +348,8 @@ def _fp8_experts(E, rows, cols, gen, zero_block_of=None, spread=4.0, zero_scales
     2^u, u ~ U(-spread, spread), per 128 x 128 block (so block scales differ),
     and one all-zero block in expert zero_block_of (the quantiser gives it
     scale 1).  zero_scales: about one block in four gets scale 0 while its
-    codes stay as drawn (the block contributes nothing)."""
+    codes stay as drawn (the block contributes nothing), and every scale of
+    expert 3 is zero (row blocks with no nonzero scale at all)."""
     codes = torch.empty(E, rows, cols, dtype=torch.uint8)
     scales = torch.empty(E, rows // 128, cols // 128, dtype=torch.float32)
     for e in range(E):
@@ -360,6 +361,8 @@ def _fp8_experts(E, rows, cols, gen, zero_block_of=None, spread=4.0, zero_scales
         codes[e], scales[e] = W.quantize_fp8_blocks(w)
         if zero_scales:
             scales[e][torch.rand(rows // 128, cols // 128, generator=gen) < 0.25] = 0.0
+            if e == 3:
+                scales[e] = 0.0
     return codes, scales
 
 
