@@ -28,6 +28,9 @@
 //               lane) and written to each of its k destination rows.  The fp8 variant quantises the row on
 //               the way (groups of 128 columns, E8M0 scales; fp8_act.h) and
 //               writes codes and scale bytes instead.
+// A mid-sized dispatch issued on its own (not beside an FFN launch) folds the
+// rank into the gather: the count kernel, then k_disp_rank_gather, which
+// ranks a group of tokens' pairs and moves their rows.
 #include <mutex>
 
 #include "fp8_act.h"
@@ -537,6 +540,75 @@ __global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__
 // flight at a time.
 constexpr int kChunks = 4;
 
+// Chunks c0 + 64 i + lane (i < kChunks) of a row of row_chunks 16-byte
+// chunks; zero past the end of the row.
+__device__ __forceinline__ void load_row_chunks(const u32x4_t* __restrict__ src, int c0, int row_chunks, int lane,
+                                                u32x4_t (&v)[kChunks]) {
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = c0 + i * 64 + lane;
+    v[i] = c < row_chunks ? src[c] : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// The chunks of v into every destination row of the token: lane j < k of
+// my_pos holds the position of pair (t, j), -1 for a pair that is not local.
+__device__ __forceinline__ void store_row_chunks(u32x4_t* __restrict__ x_perm, int c0, int row_chunks, int k,
+                                                 int my_pos, int lane, const u32x4_t (&v)[kChunks]) {
+  for (int j = 0; j < k; ++j) {
+    const int pos = __shfl(my_pos, j, kWave);
+    if (pos < 0) continue;
+    u32x4_t* dst = x_perm + static_cast<int64_t>(pos) * row_chunks;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = c0 + i * 64 + lane;
+      if (c < row_chunks) dst[c] = v[i];
+    }
+  }
+}
+
+// fp8 rows: 8 bf16 per lane per 16-byte chunk, so a 128-column group is 16
+// adjacent lanes; their amax is combined with four xor shuffles, then the
+// group's E8M0 byte and the E4M3 codes of the chunk.
+__device__ __forceinline__ void quant_row_chunks(const u32x4_t (&v)[kChunks], uint32_t (&q)[kChunks][2],
+                                                 uint32_t (&sb)[kChunks]) {
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    float f[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      f[2 * w] = __uint_as_float(v[i][w] << 16);
+      f[2 * w + 1] = __uint_as_float(v[i][w] & 0xffff0000u);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
+    sb[i] = e8m0_for_amax(m);
+    const float is = e8m0_inv_scale(sb[i]);
+    q[i][0] = fp8x4_rne(f[0] * is, f[1] * is, f[2] * is, f[3] * is);
+    q[i][1] = fp8x4_rne(f[4] * is, f[5] * is, f[6] * is, f[7] * is);
+  }
+}
+
+// Codes and scale bytes of the quantised chunks into destination row pos.
+__device__ __forceinline__ void store_q8_chunks(uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, int64_t pos,
+                                                int c0, int row_chunks, int lane, const uint32_t (&q)[kChunks][2],
+                                                const uint32_t (&sb)[kChunks]) {
+  const int64_t H = static_cast<int64_t>(row_chunks) * 8;
+  const int groups = row_chunks / 16;
+  uint8_t* dst = xq + pos * H;
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = c0 + i * 64 + lane;
+    if (c < row_chunks) {
+      *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(q[i][0], q[i][1]);
+      if ((lane & 15) == 0) xs[pos * groups + c / 16] = static_cast<uint8_t>(sb[i]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_disp_gather(const u32x4_t* __restrict__ x, int64_t T, int row_chunks,
                                                      int k, const int32_t* __restrict__ inv,
                                                      u32x4_t* __restrict__ x_perm) {
@@ -550,35 +622,18 @@ __global__ __launch_bounds__(256) void k_disp_gather(const u32x4_t* __restrict__
     const u32x4_t* src = x + t * row_chunks;
     for (int c0 = 0; c0 < row_chunks; c0 += 64 * kChunks) {
       u32x4_t v[kChunks];
-#pragma unroll
-      for (int i = 0; i < kChunks; ++i) {
-        const int c = c0 + i * 64 + lane;
-        if (c < row_chunks) v[i] = src[c];
-      }
-      for (int j = 0; j < k; ++j) {
-        const int pos = __shfl(my_pos, j, kWave);
-        if (pos < 0) continue;
-        u32x4_t* dst = x_perm + static_cast<int64_t>(pos) * row_chunks;
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-          const int c = c0 + i * 64 + lane;
-          if (c < row_chunks) dst[c] = v[i];
-        }
-      }
+      load_row_chunks(src, c0, row_chunks, lane, v);
+      store_row_chunks(x_perm, c0, row_chunks, k, my_pos, lane, v);
     }
   }
 }
 
-// fp8 gather: 8 bf16 per lane per 16-byte load, so a 128-column group is 16
-// adjacent lanes; their amax is combined with four xor shuffles.  inv == NULL
-// maps row t to row t (plain row quantisation, k = 1).
+// fp8 gather.  inv == NULL maps row t to row t (plain row quantisation, k = 1).
 __global__ __launch_bounds__(256) void k_disp_gather_q8(const u32x4_t* __restrict__ x, int64_t T, int row_chunks,
                                                         int k, const int32_t* __restrict__ inv,
                                                         uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
-  const int64_t H = static_cast<int64_t>(row_chunks) * 8;
-  const int groups = row_chunks / 16;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave; t < T; t += stride) {
     // as in the bf16 gather: pair positions in lanes j < k, tokens without a
     // local pair skipped (without inv, k = 1 and row t goes to row t)
@@ -587,43 +642,163 @@ __global__ __launch_bounds__(256) void k_disp_gather_q8(const u32x4_t* __restric
     const u32x4_t* src = x + t * row_chunks;
     for (int c0 = 0; c0 < row_chunks; c0 += 64 * kChunks) {
       u32x4_t v[kChunks];
-#pragma unroll
-      for (int i = 0; i < kChunks; ++i) {
-        const int c = c0 + i * 64 + lane;
-        v[i] = c < row_chunks ? src[c] : u32x4_t{0u, 0u, 0u, 0u};
-      }
+      load_row_chunks(src, c0, row_chunks, lane, v);
       uint32_t q[kChunks][2], sb[kChunks];
-#pragma unroll
-      for (int i = 0; i < kChunks; ++i) {
-        float f[8];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          f[2 * w] = __uint_as_float(v[i][w] << 16);
-          f[2 * w + 1] = __uint_as_float(v[i][w] & 0xffff0000u);
-        }
-        float m = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(f[j]));
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, kWave));
-        sb[i] = e8m0_for_amax(m);
-        const float is = e8m0_inv_scale(sb[i]);
-        q[i][0] = fp8x4_rne(f[0] * is, f[1] * is, f[2] * is, f[3] * is);
-        q[i][1] = fp8x4_rne(f[4] * is, f[5] * is, f[6] * is, f[7] * is);
-      }
+      quant_row_chunks(v, q, sb);
       for (int j = 0; j < k; ++j) {
         const int64_t pos = inv ? static_cast<int64_t>(__shfl(my_pos, j, kWave)) : t;
         if (pos < 0) continue;
-        uint8_t* dst = xq + pos * H;
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-          const int c = c0 + i * 64 + lane;
-          if (c < row_chunks) {
-            *reinterpret_cast<uint2*>(dst + c * 8) = make_uint2(q[i][0], q[i][1]);
-            if ((lane & 15) == 0) xs[pos * groups + c / 16] = static_cast<uint8_t>(sb[i]);
-          }
-        }
+        store_q8_chunks(xq, xs, pos, c0, row_chunks, lane, q, sb);
       }
+    }
+  }
+}
+
+// Mid-sized batches whose dispatch is issued on its own (not beside an FFN
+// launch): the rank and the row gather in one kernel after the count kernel,
+// two launches instead of three.  Workgroup g owns the kFusedTokens tokens
+// from kFusedTokens g on, one per wave, and so the pairs from
+// kFusedTokens g k on, which it ranks and moves:
+//  1. each wave reads its token's k ids and, when one of them is local,
+//     starts loading the first part of the token's row (the loads stay in
+//     flight during steps 2-4: a row does not depend on its positions);
+//  2. it sums the count kernel's block histograms (blocks of 1024 pairs) over
+//     the blocks before the block that holds its first pair, and over all of
+//     them, and counts from the ids the pairs of that block before its first
+//     pair: so it knows, per expert, the pairs before its own;
+//  3. it scans the expert totals into offsets (workgroup 0 writes counts,
+//     offsets, tile offsets and the error word);
+//  4. it ranks its pairs in pair order (ballot groups in each wave: lanes
+//     holding the same expert, rank = popcount of the lower ones; then the
+//     counts of the lower waves) and writes perm and inv;
+//  5. each wave moves its token's row to the token's positions (bf16 rows, or
+//     fp8 codes and E8M0 bytes).
+// The positions are those of the stable counting sort, as in
+// k_disp_rank_scan + k_disp_gather.
+constexpr int kFusedTokens = 16;
+constexpr int kFusedMaxK = 64;
+constexpr int64_t kFusedMaxHist = 16384;   // blocks x local experts summed by each workgroup
+
+template <bool Q8>
+__global__ __launch_bounds__(1024) void k_disp_rank_gather(
+    const int32_t* __restrict__ ids, int64_t T, int k, int e_begin, int E_loc, int64_t nb, int parts, int tile_m,
+    const int32_t* __restrict__ block_hist, const int32_t* __restrict__ block_err, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_offsets, int32_t* __restrict__ err,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, const u32x4_t* __restrict__ x, int row_chunks,
+    void* __restrict__ x_perm, uint8_t* __restrict__ xs) {
+  __shared__ int s_pre[kMidMaxELoc];                // pairs of expert e before this workgroup's first pair
+  __shared__ int s_run[kMidMaxELoc];                // pairs of expert e in all blocks, then the first position
+  __shared__ int s_wcnt[kFusedTokens][kMidMaxELoc];  // this workgroup's count per wave (token) and expert
+  __shared__ int s_wsum[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t g = blockIdx.x;
+  const int64_t t = g * kFusedTokens + wave;
+  const int64_t p_first = g * kFusedTokens * k;
+  // 1. this wave's token
+  int le = -1;
+  if (t < T && lane < k) {
+    const int e = ids[t * k + lane] - e_begin;
+    if (e >= 0 && e < E_loc) le = e;
+  }
+  const bool token_local = __ballot(le >= 0) != 0;
+  const u32x4_t* src = x + t * row_chunks;
+  u32x4_t v[kChunks];
+  if (token_local) load_row_chunks(src, 0, row_chunks, lane, v);
+  for (int e = tid; e < E_loc; e += 1024) {
+    s_pre[e] = 0;
+    s_run[e] = 0;
+  }
+  for (int i = tid; i < kFusedTokens * E_loc; i += 1024) s_wcnt[i / E_loc][i % E_loc] = 0;
+  __syncthreads();
+  // 2. pairs before this workgroup's, and the totals
+  const int64_t cb = p_first / kMidPairsPerBlock;
+  if (tid < parts * E_loc) {
+    const int e = tid % E_loc;
+    const int part = tid / E_loc;
+    const int64_t per = (nb + parts - 1) / parts;
+    const int64_t r0 = min(nb, part * per);
+    const int64_t r1 = min(nb, r0 + per);
+    constexpr int U = 8;
+    int pre = 0, tot = 0;
+    for (int64_t r = r0; r < r1; r += U) {
+      int h[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) h[u] = r + u < r1 ? block_hist[(r + u) * E_loc + e] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        tot += h[u];
+        pre += r + u < cb ? h[u] : 0;
+      }
+    }
+    if (pre) atomicAdd(&s_pre[e], pre);
+    if (tot) atomicAdd(&s_run[e], tot);
+  }
+  {
+    const int64_t q = cb * kMidPairsPerBlock + tid;   // < p_first <= T k when taken
+    if (q < p_first) {
+      const int e = ids[q] - e_begin;
+      if (e >= 0 && e < E_loc) atomicAdd(&s_pre[e], 1);
+    }
+  }
+  int any = 0;
+  if (g == 0)
+    for (int64_t q = tid; q < nb; q += 1024) any |= block_err[q];
+  any = __syncthreads_or(any);
+  // 3. offsets
+  const int cnt = tid < E_loc ? s_run[tid] : 0;
+  const int off = block_excl_scan_1024(cnt, s_wsum);
+  if (g == 0) {
+    if (tid < E_loc) {
+      counts[tid] = cnt;
+      offsets[tid] = off;
+    }
+    if (tid == E_loc - 1) offsets[E_loc] = off + cnt;
+    if (tid == 0) err[0] = any;
+  }
+  if (tile_offsets) {
+    const int tiles = (cnt + tile_m - 1) / tile_m;
+    const int toff = block_excl_scan_1024(tiles, s_wsum);
+    if (g == 0) {
+      if (tid < E_loc) tile_offsets[tid] = toff;
+      if (tid == E_loc - 1) tile_offsets[E_loc] = toff + tiles;
+    }
+  }
+  // every read of the totals is behind the scan's closing barrier
+  if (tid < E_loc) s_run[tid] = off + s_pre[tid];
+  // 4. ranks
+  const bool local = le >= 0;
+  uint64_t remaining = __ballot(local);
+  uint64_t mine = 0;
+  while (remaining) {
+    const int leader = __ffsll(static_cast<unsigned long long>(remaining)) - 1;
+    const int lead_e = __shfl(le, leader, kWave);
+    const uint64_t m = __ballot(local && le == lead_e);
+    if (local && le == lead_e) mine = m;
+    remaining &= ~m;
+  }
+  const uint64_t lower = mine & lanemask_lt();
+  if (local && lower == 0) s_wcnt[wave][le] = __popcll(mine);
+  __syncthreads();
+  int pos = -1;
+  if (local) {
+    pos = s_run[le] + __popcll(lower);
+    for (int w = 0; w < wave; ++w) pos += s_wcnt[w][le];
+    perm[pos] = static_cast<int32_t>(t * k + lane);
+  }
+  if (t < T && lane < k) inv[t * k + lane] = pos;
+  // 5. the row (no barrier from here on)
+  if (!token_local) return;
+  for (int c0 = 0; c0 < row_chunks; c0 += 64 * kChunks) {
+    if (c0 > 0) load_row_chunks(src, c0, row_chunks, lane, v);
+    if constexpr (Q8) {
+      uint32_t q[kChunks][2], sb[kChunks];
+      quant_row_chunks(v, q, sb);
+      for (int j = 0; j < k; ++j) {
+        const int pj = __shfl(pos, j, kWave);
+        if (pj >= 0) store_q8_chunks(static_cast<uint8_t*>(x_perm), xs, pj, c0, row_chunks, lane, q, sb);
+      }
+    } else {
+      store_row_chunks(static_cast<u32x4_t*>(x_perm), c0, row_chunks, k, pos, lane, v);
     }
   }
 }
@@ -702,9 +877,41 @@ moe_status launch_dispatch_recv(const DispatchArgs& a, hipStream_t s) {
 }
 
 moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
-  const moe_status st = launch_dispatch_send(a, s);
-  if (st != MOE_OK) return st;
-  return launch_dispatch_recv(a, s);
+  const int E_loc = a.e_end - a.e_begin;
+  const int64_t n_pairs = a.T * a.k;
+  const int64_t nb_mid = (n_pairs + kMidPairsPerBlock - 1) / kMidPairsPerBlock;
+  const int64_t groups = (a.T + kFusedTokens - 1) / kFusedTokens;
+  // The mid-sized path with the rank folded into the gather (two launches);
+  // beside an FFN launch the lean rank kernel and the gather run instead,
+  // and a grid cap on the comm kernels keeps the three-launch form.
+  const bool fused = !a.beside_ffn && (n_pairs > kSmallMaxPairs || E_loc > kSmallMaxELoc) &&
+                     E_loc <= kMidMaxELoc && nb_mid * E_loc <= kFusedMaxHist && a.k <= kFusedMaxK &&
+                     (a.max_blocks <= 0 || groups <= a.max_blocks);
+  if (!fused) {
+    const moe_status st = launch_dispatch_send(a, s);
+    if (st != MOE_OK) return st;
+    return launch_dispatch_recv(a, s);
+  }
+  DispWs w = carve(a.ws, n_pair_blocks(a.T, a.k), E_loc);
+  hipLaunchKernelGGL(k_disp_count<kMidPairsPerBlock>, dim3(static_cast<unsigned>(nb_mid)), dim3(kMidPairsPerBlock),
+                     0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist, w.block_err);
+  DBOMOE_CHECK_LAUNCH();
+  const int parts = static_cast<int>(std::min<int64_t>(std::max(1, 1024 / E_loc), nb_mid));
+  const int row_chunks = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
+  const int tile_m = a.tile_m > 0 ? a.tile_m : 1;
+  int32_t* tile_offsets = a.tile_m > 0 ? a.tile_offsets : nullptr;
+  if (a.x_scale)
+    hipLaunchKernelGGL(k_disp_rank_gather<true>, dim3(static_cast<unsigned>(groups)), dim3(1024), 0, s, a.ids, a.T,
+                       a.k, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist, w.block_err, a.counts, a.offsets,
+                       tile_offsets, w.err, a.perm, a.inv, static_cast<const u32x4_t*>(a.x), row_chunks, a.x_perm,
+                       a.x_scale);
+  else
+    hipLaunchKernelGGL(k_disp_rank_gather<false>, dim3(static_cast<unsigned>(groups)), dim3(1024), 0, s, a.ids,
+                       a.T, a.k, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist, w.block_err, a.counts,
+                       a.offsets, tile_offsets, w.err, a.perm, a.inv, static_cast<const u32x4_t*>(a.x), row_chunks,
+                       a.x_perm, nullptr);
+  DBOMOE_CHECK_LAUNCH();
+  return MOE_OK;
 }
 
 }  // namespace dbomoe

@@ -152,17 +152,22 @@ def test_dispatch(cid, small):
         assert C.binding.moe_get_device_error(g["ws"]) == 0
 
 
-# Three dispatch paths: up to 2048 pairs and 256 local experts one workgroup
+# Dispatch paths: up to 2048 pairs and 256 local experts one workgroup
 # counts, scans and ranks (pairs taken 1024 at a time); up to 256 local experts
 # and 65536 entries of 1024-pair block histograms, a count kernel and a rank
 # kernel that scans for itself; beyond, count, scan and rank kernels over
-# 256-pair blocks.  The shapes below cover each path, partial last blocks,
-# one local expert, non-local pairs and the boundaries between the paths.
+# 256-pair blocks.  A one-call dispatch on the middle path with at most 16384
+# histogram entries folds the rank into the gather (groups of 16
+# tokens; with k = 6 a group's pairs straddle the 1024-pair count blocks).
+# The shapes below cover each path, partial last blocks and groups, one local
+# expert, non-local pairs and the boundaries between the paths.
 @pytest.mark.parametrize("T,k,E,lo,hi", [(1, 1, 1, 0, 1), (3, 2, 5, 1, 4), (257, 6, 64, 0, 64),
                                          (64, 16, 300, 100, 300), (256, 8, 64, 0, 64),
                                          (2049, 1, 8, 0, 8), (300, 8, 256, 0, 32), (5000, 1, 1, 0, 1),
                                          (1024, 8, 64, 0, 64), (1025, 8, 64, 0, 64),
                                          (2048, 4, 256, 0, 256), (3000, 8, 256, 32, 64),
+                                         (3001, 6, 64, 0, 64), (200, 16, 64, 0, 64),
+                                         (9000, 8, 256, 0, 256),
                                          (8193, 8, 64, 0, 64), (1000, 3, 300, 0, 257),
                                          (33000, 8, 256, 0, 256)])
 @pytest.mark.parametrize("two_phase", [False, True])
