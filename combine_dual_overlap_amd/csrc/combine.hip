@@ -105,20 +105,23 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4_t* __restrict__ y, 
 }
 
 // The combine issued beside an FFN launch on the other stream.  A CU running
-// the gate/up GEMM holds two of its workgroups, which leave 64 VGPRs per SIMD
-// lane and no room for a workgroup of k_combine (up to 110 VGPRs): each of
-// those would wait for a GEMM workgroup to retire and then hold its slot.
-// This variant takes one 64-chunk block per wave and the source rows eight at
-// a time, with the row addresses and weights wave-uniform (scalar registers),
-// and is held to 64 VGPRs, so that a workgroup fits beside the GEMM's two.
-// The same products are summed in the same order as in k_combine, so the
-// output is bitwise the same.
+// the fp8-weight gate/up GEMM holds three of its workgroups (160 VGPRs per
+// lane each, one wave per SIMD each), which leave 32 VGPRs per SIMD lane; the
+// block-accumulator form holds two (216 VGPRs), which leave 80.  A workgroup
+// of k_combine (up to 110 VGPRs) fits in neither: it waits for a GEMM
+// workgroup to retire and then holds its slot.  This variant takes one
+// 64-chunk block per wave and the source rows two at a time, with the row
+// addresses and weights wave-uniform (scalar registers), in 31 VGPRs, so that
+// its workgroups fit beside the GEMM's.  (At 64 VGPRs it fitted only beside
+// two GEMM workgroups: the R1-shaped layer 0.908 -> 0.901 ms in DBO.)  The same
+// products are summed in the same order as in k_combine, so the output is
+// bitwise the same.
 template <bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(64))) void k_combine_lean(
+__global__ __launch_bounds__(256) void k_combine_lean(
     const u32x4_t* __restrict__ y, int64_t T, int row_chunks, int k, const int32_t* __restrict__ inv,
     const float* __restrict__ w, const u32x4_t* __restrict__ shared, int n_shared, u32x4_t* __restrict__ out) {
   constexpr int EPC = BF16 ? 8 : 4;
-  constexpr int G = 8;                // source rows loaded together
+  constexpr int G = 2;                // source rows loaded together
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = (row_chunks + 63) / 64;

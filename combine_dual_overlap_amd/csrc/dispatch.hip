@@ -69,29 +69,32 @@ static DispWs carve(void* ws, int64_t nb, int32_t E_loc) {
   return d;
 }
 
-// One pair per thread, PPB pairs per workgroup.
-template <int PPB>
-__global__ __launch_bounds__(PPB) void k_disp_count(const int32_t* __restrict__ ids, int64_t n_pairs,
-                                                    int E_total, int e_begin, int E_loc,
-                                                    int32_t* __restrict__ block_hist,
-                                                    int32_t* __restrict__ block_err) {
+// PPB pairs per workgroup of THREADS threads (PPB / THREADS pairs each).
+template <int PPB, int THREADS = PPB>
+__global__ __launch_bounds__(THREADS) void k_disp_count(const int32_t* __restrict__ ids, int64_t n_pairs,
+                                                        int E_total, int e_begin, int E_loc,
+                                                        int32_t* __restrict__ block_hist,
+                                                        int32_t* __restrict__ block_err) {
   __shared__ int hist[kMaxELoc];
-  for (int e = threadIdx.x; e < E_loc; e += PPB) hist[e] = 0;
+  for (int e = threadIdx.x; e < E_loc; e += THREADS) hist[e] = 0;
   __syncthreads();
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * PPB + threadIdx.x;
   int bad = 0;
-  if (p < n_pairs) {
-    const int e = ids[p];
-    if (e < 0 || e >= E_total) {
-      bad = 1;
-    } else {
-      const int le = e - e_begin;
-      if (le >= 0 && le < E_loc) atomicAdd(&hist[le], 1);
+#pragma unroll
+  for (int i = 0; i < PPB / THREADS; ++i) {
+    const int64_t p = static_cast<int64_t>(blockIdx.x) * PPB + i * THREADS + threadIdx.x;
+    if (p < n_pairs) {
+      const int e = ids[p];
+      if (e < 0 || e >= E_total) {
+        bad = 1;
+      } else {
+        const int le = e - e_begin;
+        if (le >= 0 && le < E_loc) atomicAdd(&hist[le], 1);
+      }
     }
   }
   bad = __syncthreads_or(bad);
   int32_t* out = block_hist + static_cast<int64_t>(blockIdx.x) * E_loc;
-  for (int e = threadIdx.x; e < E_loc; e += PPB) out[e] = hist[e];
+  for (int e = threadIdx.x; e < E_loc; e += THREADS) out[e] = hist[e];
   if (threadIdx.x == 0) block_err[blockIdx.x] = bad;
 }
 
@@ -336,16 +339,19 @@ __device__ __forceinline__ int block_excl_scan_256(int v, int* s_wsum) {
 }
 
 // The rank kernel of a dispatch issued beside an FFN launch on the other
-// stream.  A CU running the gate/up GEMM holds two of its workgroups, which
-// leave 64 VGPRs per SIMD lane and about 15 KB of LDS: a workgroup of
+// stream.  A CU running the fp8-weight gate/up GEMM holds three of its
+// workgroups, which leave 32 VGPRs per SIMD lane and about 14 KB of LDS (two
+// block-accumulator workgroups leave 80 VGPRs): a workgroup of
 // k_disp_rank_scan (1024 threads, 92 VGPRs, 19 KB) only starts once a CU has
-// drained.  This variant has 256 threads, at most 64 VGPRs and 6 KB of LDS, so
-// it fits beside the GEMM.  Same blocks of 1024 pairs, same results: the
-// block's pairs are ranked in four rounds of 256 in pair order, each round on
-// top of the running per-expert position the rounds before it left.
+// drained.  This variant has 256 threads, 32 VGPRs and 6 KB of LDS, so it fits
+// beside the GEMM.  Same blocks of 1024 pairs, same results: the block's pairs
+// are ranked in four rounds of 256 in pair order, each round on top of the
+// running per-expert position the rounds before it left.  The count kernel
+// before it runs 256 threads of four pairs each (12 VGPRs) for the same
+// reason, and the row gather after it k_disp_gather_lean.
 constexpr int kLeanThreads = 256;
 
-__global__ __launch_bounds__(kLeanThreads) __attribute__((amdgpu_num_vgpr(64))) void k_disp_rank_scan_lean(
+__global__ __launch_bounds__(kLeanThreads) void k_disp_rank_scan_lean(
     const int32_t* __restrict__ ids, int64_t n_pairs, int e_begin, int E_loc, int64_t nb, int parts, int tile_m,
     const int32_t* __restrict__ block_hist, const int32_t* __restrict__ block_err, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_offsets, int32_t* __restrict__ err,
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(kLeanThreads) __attribute__((amdgpu_num_vgpr(64))) 
     const int64_t per = (nb + parts - 1) / parts;
     const int64_t r0 = min(nb, part * per);
     const int64_t r1 = min(nb, r0 + per);
-    constexpr int U = 8;
+    constexpr int U = 4;
     int pre = 0, tot = 0;
     for (int64_t r = r0; r < r1; r += U) {
       int v[U];
@@ -542,10 +548,11 @@ constexpr int kChunks = 4;
 
 // Chunks c0 + 64 i + lane (i < kChunks) of a row of row_chunks 16-byte
 // chunks; zero past the end of the row.
+template <int CH = kChunks>
 __device__ __forceinline__ void load_row_chunks(const u32x4_t* __restrict__ src, int c0, int row_chunks, int lane,
-                                                u32x4_t (&v)[kChunks]) {
+                                                u32x4_t (&v)[CH]) {
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
+  for (int i = 0; i < CH; ++i) {
     const int c = c0 + i * 64 + lane;
     v[i] = c < row_chunks ? src[c] : u32x4_t{0u, 0u, 0u, 0u};
   }
@@ -553,14 +560,15 @@ __device__ __forceinline__ void load_row_chunks(const u32x4_t* __restrict__ src,
 
 // The chunks of v into every destination row of the token: lane j < k of
 // my_pos holds the position of pair (t, j), -1 for a pair that is not local.
+template <int CH = kChunks>
 __device__ __forceinline__ void store_row_chunks(u32x4_t* __restrict__ x_perm, int c0, int row_chunks, int k,
-                                                 int my_pos, int lane, const u32x4_t (&v)[kChunks]) {
+                                                 int my_pos, int lane, const u32x4_t (&v)[CH]) {
   for (int j = 0; j < k; ++j) {
     const int pos = __shfl(my_pos, j, kWave);
     if (pos < 0) continue;
     u32x4_t* dst = x_perm + static_cast<int64_t>(pos) * row_chunks;
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
+    for (int i = 0; i < CH; ++i) {
       const int c = c0 + i * 64 + lane;
       if (c < row_chunks) dst[c] = v[i];
     }
@@ -609,9 +617,9 @@ __device__ __forceinline__ void store_q8_chunks(uint8_t* __restrict__ xq, uint8_
   }
 }
 
-__global__ __launch_bounds__(256) void k_disp_gather(const u32x4_t* __restrict__ x, int64_t T, int row_chunks,
-                                                     int k, const int32_t* __restrict__ inv,
-                                                     u32x4_t* __restrict__ x_perm) {
+template <int CH>
+__device__ __forceinline__ void gather_rows(const u32x4_t* __restrict__ x, int64_t T, int row_chunks, int k,
+                                            const int32_t* __restrict__ inv, u32x4_t* __restrict__ x_perm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave; t < T; t += stride) {
@@ -620,12 +628,27 @@ __global__ __launch_bounds__(256) void k_disp_gather(const u32x4_t* __restrict__
     const int my_pos = lane < k ? inv[t * k + lane] : -1;
     if (__ballot(my_pos >= 0) == 0) continue;
     const u32x4_t* src = x + t * row_chunks;
-    for (int c0 = 0; c0 < row_chunks; c0 += 64 * kChunks) {
-      u32x4_t v[kChunks];
-      load_row_chunks(src, c0, row_chunks, lane, v);
-      store_row_chunks(x_perm, c0, row_chunks, k, my_pos, lane, v);
+    for (int c0 = 0; c0 < row_chunks; c0 += 64 * CH) {
+      u32x4_t v[CH];
+      load_row_chunks<CH>(src, c0, row_chunks, lane, v);
+      store_row_chunks<CH>(x_perm, c0, row_chunks, k, my_pos, lane, v);
     }
   }
+}
+
+__global__ __launch_bounds__(256) void k_disp_gather(const u32x4_t* __restrict__ x, int64_t T, int row_chunks,
+                                                     int k, const int32_t* __restrict__ inv,
+                                                     u32x4_t* __restrict__ x_perm) {
+  gather_rows<kChunks>(x, T, row_chunks, k, inv, x_perm);
+}
+
+// The row gather issued beside an FFN launch: two chunks per lane in flight
+// (26 VGPRs), so its workgroups fit in the 32 VGPRs per lane that the GEMM's
+// resident workgroups leave free.
+__global__ __launch_bounds__(256) void k_disp_gather_lean(
+    const u32x4_t* __restrict__ x, int64_t T, int row_chunks, int k, const int32_t* __restrict__ inv,
+    u32x4_t* __restrict__ x_perm) {
+  gather_rows<2>(x, T, row_chunks, k, inv, x_perm);
 }
 
 // fp8 gather.  inv == NULL maps row t to row t (plain row quantisation, k = 1).
@@ -654,6 +677,19 @@ __global__ __launch_bounds__(256) void k_disp_gather_q8(const u32x4_t* __restric
   }
 }
 
+// Exclusive scan of v over a workgroup of NW waves.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan_waves(int v, int* s_wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wsum[w];
+  __syncthreads();
+  return base + incl - v;
+}
+
 // Mid-sized batches whose dispatch is issued on its own (not beside an FFN
 // launch): the rank and the row gather in one kernel after the count kernel,
 // two launches instead of three.  Workgroup g owns the kFusedTokens tokens
@@ -675,12 +711,14 @@ __global__ __launch_bounds__(256) void k_disp_gather_q8(const u32x4_t* __restric
 //     fp8 codes and E8M0 bytes).
 // The positions are those of the stable counting sort, as in
 // k_disp_rank_scan + k_disp_gather.
+// (4 or 8 tokens per workgroup measured the same in the layer)
 constexpr int kFusedTokens = 16;
+constexpr int kFusedThreads = 64 * kFusedTokens;
 constexpr int kFusedMaxK = 64;
 constexpr int64_t kFusedMaxHist = 16384;   // blocks x local experts summed by each workgroup
 
 template <bool Q8>
-__global__ __launch_bounds__(1024) void k_disp_rank_gather(
+__global__ __launch_bounds__(kFusedThreads) void k_disp_rank_gather(
     const int32_t* __restrict__ ids, int64_t T, int k, int e_begin, int E_loc, int64_t nb, int parts, int tile_m,
     const int32_t* __restrict__ block_hist, const int32_t* __restrict__ block_err, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_offsets, int32_t* __restrict__ err,
@@ -704,11 +742,11 @@ __global__ __launch_bounds__(1024) void k_disp_rank_gather(
   const u32x4_t* src = x + t * row_chunks;
   u32x4_t v[kChunks];
   if (token_local) load_row_chunks(src, 0, row_chunks, lane, v);
-  for (int e = tid; e < E_loc; e += 1024) {
+  for (int e = tid; e < E_loc; e += kFusedThreads) {
     s_pre[e] = 0;
     s_run[e] = 0;
   }
-  for (int i = tid; i < kFusedTokens * E_loc; i += 1024) s_wcnt[i / E_loc][i % E_loc] = 0;
+  for (int i = tid; i < kFusedTokens * E_loc; i += kFusedThreads) s_wcnt[i / E_loc][i % E_loc] = 0;
   __syncthreads();
   // 2. pairs before this workgroup's, and the totals
   const int64_t cb = p_first / kMidPairsPerBlock;
@@ -733,20 +771,17 @@ __global__ __launch_bounds__(1024) void k_disp_rank_gather(
     if (pre) atomicAdd(&s_pre[e], pre);
     if (tot) atomicAdd(&s_run[e], tot);
   }
-  {
-    const int64_t q = cb * kMidPairsPerBlock + tid;   // < p_first <= T k when taken
-    if (q < p_first) {
-      const int e = ids[q] - e_begin;
-      if (e >= 0 && e < E_loc) atomicAdd(&s_pre[e], 1);
-    }
+  for (int64_t q = cb * kMidPairsPerBlock + tid; q < p_first; q += kFusedThreads) {   // p_first <= T k
+    const int e = ids[q] - e_begin;
+    if (e >= 0 && e < E_loc) atomicAdd(&s_pre[e], 1);
   }
   int any = 0;
   if (g == 0)
-    for (int64_t q = tid; q < nb; q += 1024) any |= block_err[q];
+    for (int64_t q = tid; q < nb; q += kFusedThreads) any |= block_err[q];
   any = __syncthreads_or(any);
   // 3. offsets
   const int cnt = tid < E_loc ? s_run[tid] : 0;
-  const int off = block_excl_scan_1024(cnt, s_wsum);
+  const int off = block_excl_scan_waves<kFusedTokens>(cnt, s_wsum);
   if (g == 0) {
     if (tid < E_loc) {
       counts[tid] = cnt;
@@ -757,7 +792,7 @@ __global__ __launch_bounds__(1024) void k_disp_rank_gather(
   }
   if (tile_offsets) {
     const int tiles = (cnt + tile_m - 1) / tile_m;
-    const int toff = block_excl_scan_1024(tiles, s_wsum);
+    const int toff = block_excl_scan_waves<kFusedTokens>(tiles, s_wsum);
     if (g == 0) {
       if (tid < E_loc) tile_offsets[tid] = toff;
       if (tid == E_loc - 1) tile_offsets[E_loc] = toff + tiles;
@@ -811,6 +846,10 @@ static moe_status launch_gather(const DispatchArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_disp_gather_q8, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                        static_cast<const u32x4_t*>(a.x), a.T, row_chunks, a.k, a.inv,
                        static_cast<uint8_t*>(a.x_perm), a.x_scale);
+  } else if (a.beside_ffn) {
+    hipLaunchKernelGGL(k_disp_gather_lean, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       static_cast<const u32x4_t*>(a.x), a.T, row_chunks, a.k, a.inv,
+                       static_cast<u32x4_t*>(a.x_perm));
   } else {
     hipLaunchKernelGGL(k_disp_gather, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                        static_cast<const u32x4_t*>(a.x), a.T, row_chunks, a.k, a.inv,
@@ -834,9 +873,14 @@ moe_status launch_dispatch_send(const DispatchArgs& a, hipStream_t s) {
   }
   const int64_t nb_mid = (n_pairs + kMidPairsPerBlock - 1) / kMidPairsPerBlock;
   if (E_loc <= kMidMaxELoc && nb_mid * E_loc <= kMidMaxHist) {
-    hipLaunchKernelGGL(k_disp_count<kMidPairsPerBlock>, dim3(static_cast<unsigned>(nb_mid)),
-                       dim3(kMidPairsPerBlock), 0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist,
-                       w.block_err);
+    if (a.beside_ffn)
+      hipLaunchKernelGGL((k_disp_count<kMidPairsPerBlock, kLeanThreads>), dim3(static_cast<unsigned>(nb_mid)),
+                         dim3(kLeanThreads), 0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist,
+                         w.block_err);
+    else
+      hipLaunchKernelGGL(k_disp_count<kMidPairsPerBlock>, dim3(static_cast<unsigned>(nb_mid)),
+                         dim3(kMidPairsPerBlock), 0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist,
+                         w.block_err);
     DBOMOE_CHECK_LAUNCH();
     const int nt = a.beside_ffn ? kLeanThreads : 1024;
     const int parts = static_cast<int>(std::min<int64_t>(std::max(1, nt / E_loc), nb_mid));
@@ -896,17 +940,17 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_disp_count<kMidPairsPerBlock>, dim3(static_cast<unsigned>(nb_mid)), dim3(kMidPairsPerBlock),
                      0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist, w.block_err);
   DBOMOE_CHECK_LAUNCH();
-  const int parts = static_cast<int>(std::min<int64_t>(std::max(1, 1024 / E_loc), nb_mid));
+  const int parts = static_cast<int>(std::min<int64_t>(std::max(1, kFusedThreads / E_loc), nb_mid));
   const int row_chunks = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
   const int tile_m = a.tile_m > 0 ? a.tile_m : 1;
   int32_t* tile_offsets = a.tile_m > 0 ? a.tile_offsets : nullptr;
   if (a.x_scale)
-    hipLaunchKernelGGL(k_disp_rank_gather<true>, dim3(static_cast<unsigned>(groups)), dim3(1024), 0, s, a.ids, a.T,
+    hipLaunchKernelGGL(k_disp_rank_gather<true>, dim3(static_cast<unsigned>(groups)), dim3(kFusedThreads), 0, s, a.ids, a.T,
                        a.k, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist, w.block_err, a.counts, a.offsets,
                        tile_offsets, w.err, a.perm, a.inv, static_cast<const u32x4_t*>(a.x), row_chunks, a.x_perm,
                        a.x_scale);
   else
-    hipLaunchKernelGGL(k_disp_rank_gather<false>, dim3(static_cast<unsigned>(groups)), dim3(1024), 0, s, a.ids,
+    hipLaunchKernelGGL(k_disp_rank_gather<false>, dim3(static_cast<unsigned>(groups)), dim3(kFusedThreads), 0, s, a.ids,
                        a.T, a.k, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist, w.block_err, a.counts,
                        a.offsets, tile_offsets, w.err, a.perm, a.inv, static_cast<const u32x4_t*>(a.x), row_chunks,
                        a.x_perm, nullptr);
