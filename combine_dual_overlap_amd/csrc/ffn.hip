@@ -46,8 +46,13 @@ static bool k_multiple_of(const GemmParams& g, int bk) {
   return g.g[0].K % bk == 0 && (g.rows1 == 0 || g.g[1].K % bk == 0);
 }
 
+// K blocks of the launch's routed group within what k_gemm_fp8w stages per
+// scale row.
+static bool fp8w_fits(const GemmParams& g) { return g.g[0].K / 128 <= kW8MaxKBlocks; }
+
 template <int MODE, bool FP8>
-static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g, bool full_tiles = false) {
+static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g, bool full_tiles = false,
+                        bool wide = false) {
   // bf16 weights, 128-row tiles: activation and weight tiles staged by LDS
   // DMA (bitwise equal to the register-staged kernel; measured
   // standalone on the skewed-layer shapes: gate/up 401 -> 367 us, down 217 ->
@@ -80,8 +85,18 @@ static void launch_mfma(int bm, dim3 grid, hipStream_t s, const GemmParams& g, b
   // (gate/up 258 -> 285 us), so it keeps the block accumulator and three
   // stages.  Tiles of 64 and 128 rows of one launch take the same arithmetic,
   // so the row tile does not change the result.
-  if (FP8 && (bm == 64 || bm == 128) && g.rows1 == 0 && g.g[0].K / 128 <= kW8MaxKBlocks) {
-    if (full_tiles) {
+  // wide (128-row gate/up tiles with the block accumulator, i.e. the
+  // weight-streaming R1-shaped share): tiles of 256 weight rows (128 gate + 128
+  // up), 8 waves of 64 x 64, a four-stage ring (128 KB, one workgroup per CU):
+  // the same waves and weight bytes in flight per CU as two 128-row tiles,
+  // with half the activation re-reads (each expert's rows are read by 16
+  // column tiles instead of 32).  R1-shaped gate/up 252 -> 233 us, layer
+  // (DBO) 0.886 -> 0.840 ms; three stages 235 us.
+  if (FP8 && (bm == 64 || bm == 128) && g.rows1 == 0 && fp8w_fits(g)) {
+    if (wide && MODE == MODE_GATEUP) {
+      if constexpr (MODE == MODE_GATEUP)
+        hipLaunchKernelGGL((k_gemm_fp8w<MODE, 128, 2, 4, 4, false, 256>), grid, dim3(512), 0, s, g);
+    } else if (full_tiles) {
       if (bm == 128)
         hipLaunchKernelGGL((k_gemm_fp8w<MODE, 128, 2, 2, 2, true>), grid, dim3(256), 0, s, g);
       else
@@ -347,9 +362,16 @@ moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   const bool fp8_launch = fp8 && a.cap_rows > 0;
 
   const bool full_tiles = a.rows_hint >= 128;
+  // 256-wide gate/up tiles for the 128-row block-accumulator launches (see launch_mfma)
+  const bool wide = fp8_launch && !full_tiles && bm == 128 && a.rows1 == 0 && fp8w_fits(p1);
+  dim3 grid1w = grid1;
+  if (wide) {
+    p1.g[0].n_tiles = p1.g[0].N / 128;
+    grid1w = dim3(static_cast<unsigned>(gemm_grid(tiles_max(bm, a.cap_rows, a.E_loc, dense, p1.g[0].n_tiles, 0, 0, 0))));
+  }
   if (a.t0 && hipEventRecord(a.t0, s) != hipSuccess) return MOE_ERR_HIP;
   if (fp8_launch)
-    launch_mfma<MODE_GATEUP, true>(bm, grid1, s, p1, full_tiles);
+    launch_mfma<MODE_GATEUP, true>(bm, grid1w, s, p1, full_tiles, wide);
   else
     launch_mfma<MODE_GATEUP, false>(bm, grid1, s, p1);
   DBOMOE_CHECK_LAUNCH();

@@ -34,9 +34,10 @@
 // K order (every tile shape of this kernel uses this one, so they agree bit
 // for bit).
 //
-// Tile: BM (64 or 128) rows x 128 weight rows (gate/up: 64 gate + the 64
-// matching up rows), WAVES_M x WAVES_N waves (2 x 2 or 2 x 4), each a block of
-// 16x16x32 bf16 MFMAs.  Group 0 (routed experts) only.
+// Tile: BM (64 or 128) rows x BN (128 or 256) weight rows (gate/up: BN/2
+// gate + the BN/2 matching up rows; a 256-row down tile spans two scale row
+// blocks, each wave's columns within one), WAVES_M x WAVES_N waves (2 x 2 or
+// 2 x 4), each a block of 16x16x32 bf16 MFMAs.  Group 0 (routed experts) only.
 #pragma once
 
 #include "gemm_mfma.h"
@@ -85,20 +86,21 @@ __device__ __forceinline__ void wait_dmas(int n) {
 
 // K blocks of one tile's scale rows (one 64-lane dword DMA per row)
 constexpr int kW8MaxKBlocks = 64;
-template <int BM, int NBUF> struct W8Lds {
+template <int BM, int NBUF, int BN = kBN> struct W8Lds {
   static constexpr int A = BM * kBK * 2;                       // activation stage
-  static constexpr int B = kBN * kBK;                          // fp8 weight stage
+  static constexpr int B = BN * kBK;                           // fp8 weight stage
   static constexpr int S = 2 * kW8MaxKBlocks * 4;              // two scale rows
   static constexpr int bytes = NBUF * (A + B) + S;
 };
 
-template <int MODE, int BM, int WAVES_M, int WAVES_N, int NBUF, bool ONE_ACC>
+template <int MODE, int BM, int WAVES_M, int WAVES_N, int NBUF, bool ONE_ACC, int BN>
 __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc& t, const GemmParams& p,
                                                uint8_t* lds) {
-  constexpr int BN = kBN, BK = kBK, NW = WAVES_M * WAVES_N;
+  static_assert(BN == 128 || BN == 256, "128 or 256 weight rows");
+  constexpr int BK = kBK, NW = WAVES_M * WAVES_N;
   using S = TileShape<BM, WAVES_M, WAVES_N, BN>;
   constexpr int TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
-  constexpr int A_BYTES = W8Lds<BM, NBUF>::A, B_BYTES = W8Lds<BM, NBUF>::B;
+  constexpr int A_BYTES = W8Lds<BM, NBUF, BN>::A, B_BYTES = W8Lds<BM, NBUF, BN>::B;
   constexpr int NQA = BM / 8 / NW;           // activation DMAs per wave per stage (8 rows each)
   constexpr int NQB = BN / 16 / NW;          // weight DMAs per wave per stage (16 rows each)
   constexpr int NDMA = NQA + NQB;
@@ -155,7 +157,7 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
     srow1 = se + static_cast<size_t>((g.N + nt * (BN / 2)) / 128) * kblocks;
   } else {
     srow0 = se + static_cast<size_t>((nt * BN) / 128) * kblocks;
-    srow1 = srow0;
+    srow1 = BN == 256 ? srow0 + kblocks : srow0;   // a 256-row tile spans two row blocks
   }
   const float* sS = reinterpret_cast<const float*>(lds + NBUF * (A_BYTES + B_BYTES));
   // Every load the compiler issued has completed: inside the loop only the
@@ -188,7 +190,12 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
   // the accumulator is expressed in and whether the current block's is nonzero
   float unit[2] = {1.f, 1.f};
   uint32_t code_mask[2] = {~0u, ~0u};
-  auto half = [](int tn) { return (MODE == MODE_GATEUP && tn >= TN / 2) ? 1 : 0; };
+  // the scale row of fragment tn: gate or up half of a gate/up tile, or the
+  // 128-row block of a 256-row down tile that the wave's columns fall in
+  auto half = [&](int tn) {
+    if constexpr (MODE == MODE_GATEUP) return tn >= TN / 2 ? 1 : 0;
+    else return BN == 256 ? (wn * WN) / 128 : 0;
+  };
   const int frag_row = lane & 15, q = lane >> 4;
   const int tm_valid = __builtin_amdgcn_readfirstlane(
       max(0, min(TM, (t.rows - t.m_off - wm * WM + 15) / 16)));
@@ -264,7 +271,7 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
       if (decltype(full)::value || tm < tm_valid)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const float sc = (MODE == MODE_GATEUP && tn >= TN / 2) ? s[1] : s[0];
+          const float sc = s[half(tn)];
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[tm][tn][r] = __builtin_fmaf(sc, blk[tm][tn][r], acc[tm][tn][r]);
         }
@@ -336,23 +343,23 @@ __device__ __forceinline__ void gemm_tile_fp8w(const GemmGroup& g, const TileLoc
 // Waves per SIMD a shape runs at: workgroups per CU from its LDS (160 KB per
 // CU) times its waves, over 4 SIMDs (at most 4: the register budget of a wave
 // is 512 / waves per SIMD).
-template <int BM, int NW, int NBUF> struct W8Occ {
-  static constexpr int wgs = (160 * 1024) / W8Lds<BM, NBUF>::bytes;
+template <int BM, int NW, int NBUF, int BN = kBN> struct W8Occ {
+  static constexpr int wgs = (160 * 1024) / W8Lds<BM, NBUF, BN>::bytes;
   static constexpr int w = wgs * NW / 4;
   static constexpr int value = w < 1 ? 1 : w > 4 ? 4 : w;
 };
 
 // Group 0 only (a launch without a dense group of shared experts); K a
 // multiple of 128 with at most kW8MaxKBlocks blocks.
-template <int MODE, int BM, int WAVES_M = 2, int WAVES_N = 2, int NBUF = 3, bool ONE_ACC = false>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, (W8Occ<BM, WAVES_M * WAVES_N, NBUF>::value))
+template <int MODE, int BM, int WAVES_M = 2, int WAVES_N = 2, int NBUF = 3, bool ONE_ACC = false, int BN = kBN>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, (W8Occ<BM, WAVES_M * WAVES_N, NBUF, BN>::value))
 void k_gemm_fp8w(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[W8Lds<BM, NBUF>::bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[W8Lds<BM, NBUF, BN>::bytes];
   int* s_loc = reinterpret_cast<int*>(lds);
   TileLoc t;
   if (!locate_tile<BM>(p, s_loc, t)) return;
   __syncthreads();                                  // s_loc read by all before the ring is filled
-  gemm_tile_fp8w<MODE, BM, WAVES_M, WAVES_N, NBUF, ONE_ACC>(p.g[0], t, p, lds);
+  gemm_tile_fp8w<MODE, BM, WAVES_M, WAVES_N, NBUF, ONE_ACC, BN>(p.g[0], t, p, lds);
 }
 
 }  // namespace dbomoe
