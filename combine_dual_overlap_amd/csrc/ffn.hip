@@ -342,7 +342,7 @@ moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
     p2.g[1] = gd;
     p2.E1 = n_ch;
   }
-  if (bm != 16) {                // column tiles of the LDS-tiled kernel's width
+  {                              // column tiles of the LDS-tiled kernel's width
     const int bn = col_tile_rows(bm);
     p1.g[0].n_tiles = p1.g[0].N / (bn / 2);
     p2.g[0].n_tiles = p2.g[0].N / bn;
