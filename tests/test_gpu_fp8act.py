@@ -127,6 +127,37 @@ def test_dispatch_fp8_matches_oracle(cid):
     assert np.array_equal(xs.cpu().numpy()[:M].astype(np.int64), e + 127)
 
 
+# The quantising gather on each dispatch path: one workgroup (small), the
+# rank folded into the gather (groups of 16 tokens, the last one partial, with
+# k = 6 a group's pairs straddling the 1024-pair count blocks), and the
+# separate count, scan and rank kernels (more than 256 local experts).
+@pytest.mark.parametrize("T,k,E,lo,hi", [(200, 6, 64, 0, 64), (1001, 6, 64, 0, 64), (3001, 8, 256, 32, 96),
+                                         (700, 4, 300, 0, 257)])
+def test_dispatch_fp8_shapes(T, k, E, lo, hi):
+    B = _B()
+    rng = np.random.default_rng(T * 7 + k)
+    H = 256
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = (torch.randn(T, H) * torch.exp2(torch.randint(-6, 7, (T, 1)).float())).to(torch.bfloat16)
+    ref = O.dispatch_ref(ids, lo, hi)
+    E_loc, M = hi - lo, ref["M"]
+    i32 = lambda n: torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    counts, offsets, perm, inv = i32(E_loc), i32(E_loc + 1), i32(T * k), i32(T * k)
+    xq = torch.zeros(T * k, H, dtype=torch.uint8, device="cuda")
+    xs = torch.zeros(T * k, H // 128, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(B.moe_dispatch_workspace_size(T, k, E_loc), dtype=torch.uint8, device="cuda")
+    print(f"fp8 dispatch T={T} k={k} E={E} local [{lo}, {hi})", flush=True)
+    B.moe_dispatch_fp8(x.cuda(), torch.from_numpy(ids).cuda(), E, lo, hi, counts, offsets, perm, inv, xq, xs, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(perm.cpu().numpy()[:M], ref["perm"])
+    assert np.array_equal(inv.cpu().numpy(), ref["inv"])
+    codes, e = O.quant_rows_fp8(O.decode(W.bits(x), "bf16")[ref["perm"] // k])
+    assert np.array_equal(xq.cpu().numpy()[:M], codes)
+    assert np.array_equal(xs.cpu().numpy()[:M].astype(np.int64), e + 127)
+
+
 def test_dispatch_send_recv_fp8_equals_one_call():
     B = _B()
     inp, ov = inputs(3, True)
