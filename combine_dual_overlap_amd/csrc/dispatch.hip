@@ -692,9 +692,9 @@ __device__ __forceinline__ int block_excl_scan_waves(int v, int* s_wsum) {
 
 // Mid-sized batches whose dispatch is issued on its own (not beside an FFN
 // launch): the rank and the row gather in one kernel after the count kernel,
-// two launches instead of three.  Workgroup g owns the kFusedTokens tokens
-// from kFusedTokens g on, one per wave, and so the pairs from
-// kFusedTokens g k on, which it ranks and moves:
+// two launches instead of three.  Workgroup g owns the TOK tokens from TOK g
+// on, one per wave, and so the pairs from TOK g k on, which it ranks and
+// moves:
 //  1. each wave reads its token's k ids and, when one of them is local,
 //     starts loading the first part of the token's row (the loads stay in
 //     flight during steps 2-4: a row does not depend on its positions);
@@ -711,14 +711,14 @@ __device__ __forceinline__ int block_excl_scan_waves(int v, int* s_wsum) {
 //     fp8 codes and E8M0 bytes).
 // The positions are those of the stable counting sort, as in
 // k_disp_rank_scan + k_disp_gather.
-// (4 or 8 tokens per workgroup measured the same in the layer)
-constexpr int kFusedTokens = 16;
-constexpr int kFusedThreads = 64 * kFusedTokens;
+// TOK = 16 tokens per workgroup; 4 when that leaves fewer than 256
+// workgroups (the R1-shaped share's 2048-token microbatches: 128 workgroups
+// of 16 left half the CUs idle; dispatch step 22.4-23.4 -> 19.4-19.5 us)
 constexpr int kFusedMaxK = 64;
 constexpr int64_t kFusedMaxHist = 16384;   // blocks x local experts summed by each workgroup
 
-template <bool Q8>
-__global__ __launch_bounds__(kFusedThreads) void k_disp_rank_gather(
+template <bool Q8, int TOK>
+__global__ __launch_bounds__(64 * TOK) void k_disp_rank_gather(
     const int32_t* __restrict__ ids, int64_t T, int k, int e_begin, int E_loc, int64_t nb, int parts, int tile_m,
     const int32_t* __restrict__ block_hist, const int32_t* __restrict__ block_err, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_offsets, int32_t* __restrict__ err,
@@ -726,12 +726,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_disp_rank_gather(
     void* __restrict__ x_perm, uint8_t* __restrict__ xs) {
   __shared__ int s_pre[kMidMaxELoc];                // pairs of expert e before this workgroup's first pair
   __shared__ int s_run[kMidMaxELoc];                // pairs of expert e in all blocks, then the first position
-  __shared__ int s_wcnt[kFusedTokens][kMidMaxELoc];  // this workgroup's count per wave (token) and expert
+  constexpr int kThreads = 64 * TOK;
+  __shared__ int s_wcnt[TOK][kMidMaxELoc];  // this workgroup's count per wave (token) and expert
   __shared__ int s_wsum[32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t g = blockIdx.x;
-  const int64_t t = g * kFusedTokens + wave;
-  const int64_t p_first = g * kFusedTokens * k;
+  const int64_t t = g * TOK + wave;
+  const int64_t p_first = g * TOK * k;
   // 1. this wave's token
   int le = -1;
   if (t < T && lane < k) {
@@ -742,11 +743,11 @@ __global__ __launch_bounds__(kFusedThreads) void k_disp_rank_gather(
   const u32x4_t* src = x + t * row_chunks;
   u32x4_t v[kChunks];
   if (token_local) load_row_chunks(src, 0, row_chunks, lane, v);
-  for (int e = tid; e < E_loc; e += kFusedThreads) {
+  for (int e = tid; e < E_loc; e += kThreads) {
     s_pre[e] = 0;
     s_run[e] = 0;
   }
-  for (int i = tid; i < kFusedTokens * E_loc; i += kFusedThreads) s_wcnt[i / E_loc][i % E_loc] = 0;
+  for (int i = tid; i < TOK * E_loc; i += kThreads) s_wcnt[i / E_loc][i % E_loc] = 0;
   __syncthreads();
   // 2. pairs before this workgroup's, and the totals
   const int64_t cb = p_first / kMidPairsPerBlock;
@@ -771,17 +772,17 @@ __global__ __launch_bounds__(kFusedThreads) void k_disp_rank_gather(
     if (pre) atomicAdd(&s_pre[e], pre);
     if (tot) atomicAdd(&s_run[e], tot);
   }
-  for (int64_t q = cb * kMidPairsPerBlock + tid; q < p_first; q += kFusedThreads) {   // p_first <= T k
+  for (int64_t q = cb * kMidPairsPerBlock + tid; q < p_first; q += kThreads) {   // p_first <= T k
     const int e = ids[q] - e_begin;
     if (e >= 0 && e < E_loc) atomicAdd(&s_pre[e], 1);
   }
   int any = 0;
   if (g == 0)
-    for (int64_t q = tid; q < nb; q += kFusedThreads) any |= block_err[q];
+    for (int64_t q = tid; q < nb; q += kThreads) any |= block_err[q];
   any = __syncthreads_or(any);
   // 3. offsets
   const int cnt = tid < E_loc ? s_run[tid] : 0;
-  const int off = block_excl_scan_waves<kFusedTokens>(cnt, s_wsum);
+  const int off = block_excl_scan_waves<TOK>(cnt, s_wsum);
   if (g == 0) {
     if (tid < E_loc) {
       counts[tid] = cnt;
@@ -792,7 +793,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_disp_rank_gather(
   }
   if (tile_offsets) {
     const int tiles = (cnt + tile_m - 1) / tile_m;
-    const int toff = block_excl_scan_waves<kFusedTokens>(tiles, s_wsum);
+    const int toff = block_excl_scan_waves<TOK>(tiles, s_wsum);
     if (g == 0) {
       if (tid < E_loc) tile_offsets[tid] = toff;
       if (tid == E_loc - 1) tile_offsets[E_loc] = toff + tiles;
@@ -924,7 +925,8 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int E_loc = a.e_end - a.e_begin;
   const int64_t n_pairs = a.T * a.k;
   const int64_t nb_mid = (n_pairs + kMidPairsPerBlock - 1) / kMidPairsPerBlock;
-  const int64_t groups = (a.T + kFusedTokens - 1) / kFusedTokens;
+  const int tok = (a.T + 15) / 16 >= 256 ? 16 : 4;
+  const int64_t groups = (a.T + tok - 1) / tok;
   // The mid-sized path with the rank folded into the gather (two launches);
   // beside an FFN launch the lean rank kernel and the gather run instead,
   // and a grid cap on the comm kernels keeps the three-launch form.
@@ -940,20 +942,27 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_disp_count<kMidPairsPerBlock>, dim3(static_cast<unsigned>(nb_mid)), dim3(kMidPairsPerBlock),
                      0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist, w.block_err);
   DBOMOE_CHECK_LAUNCH();
-  const int parts = static_cast<int>(std::min<int64_t>(std::max(1, kFusedThreads / E_loc), nb_mid));
+  const int parts = static_cast<int>(std::min<int64_t>(std::max(1, 64 * tok / E_loc), nb_mid));
   const int row_chunks = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
   const int tile_m = a.tile_m > 0 ? a.tile_m : 1;
   int32_t* tile_offsets = a.tile_m > 0 ? a.tile_offsets : nullptr;
-  if (a.x_scale)
-    hipLaunchKernelGGL(k_disp_rank_gather<true>, dim3(static_cast<unsigned>(groups)), dim3(kFusedThreads), 0, s, a.ids, a.T,
-                       a.k, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist, w.block_err, a.counts, a.offsets,
-                       tile_offsets, w.err, a.perm, a.inv, static_cast<const u32x4_t*>(a.x), row_chunks, a.x_perm,
-                       a.x_scale);
-  else
-    hipLaunchKernelGGL(k_disp_rank_gather<false>, dim3(static_cast<unsigned>(groups)), dim3(kFusedThreads), 0, s, a.ids,
-                       a.T, a.k, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist, w.block_err, a.counts,
-                       a.offsets, tile_offsets, w.err, a.perm, a.inv, static_cast<const u32x4_t*>(a.x), row_chunks,
-                       a.x_perm, nullptr);
+  auto launch_fused = [&](auto q8, auto tk) {
+    constexpr bool Q8 = decltype(q8)::value;
+    constexpr int TOK = decltype(tk)::value;
+    hipLaunchKernelGGL((k_disp_rank_gather<Q8, TOK>), dim3(static_cast<unsigned>(groups)), dim3(64 * TOK), 0, s,
+                       a.ids, a.T, a.k, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist, w.block_err,
+                       a.counts, a.offsets, tile_offsets, w.err, a.perm, a.inv, static_cast<const u32x4_t*>(a.x),
+                       row_chunks, a.x_perm, Q8 ? a.x_scale : nullptr);
+  };
+  using T16 = std::integral_constant<int, 16>;
+  using T4 = std::integral_constant<int, 4>;
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  if (a.x_scale) {
+    if (tok == 16) launch_fused(Yes{}, T16{}); else launch_fused(Yes{}, T4{});
+  } else {
+    if (tok == 16) launch_fused(No{}, T16{}); else launch_fused(No{}, T4{});
+  }
   DBOMOE_CHECK_LAUNCH();
   return MOE_OK;
 }
