@@ -28,9 +28,10 @@
 //               lane) and written to each of its k destination rows.  The fp8 variant quantises the row on
 //               the way (groups of 128 columns, E8M0 scales; fp8_act.h) and
 //               writes codes and scale bytes instead.
-// A mid-sized dispatch issued on its own (not beside an FFN launch) folds the
-// rank into the gather: the count kernel, then k_disp_rank_gather, which
-// ranks a group of tokens' pairs and moves their rows.
+// A dispatch issued on its own (not beside an FFN launch) folds the rank into
+// the gather: k_disp_rank_gather ranks a group of tokens' pairs and moves their
+// rows, after the count kernel for mid-sized batches, alone for small ones
+// (each workgroup then counts all the pairs from the ids).
 #include <mutex>
 
 #include "fp8_act.h"
@@ -717,9 +718,10 @@ __device__ __forceinline__ int block_excl_scan_waves(int v, int* s_wsum) {
 constexpr int kFusedMaxK = 64;
 constexpr int64_t kFusedMaxHist = 16384;   // blocks x local experts summed by each workgroup
 
-template <bool Q8, int TOK>
+template <bool Q8, int TOK, bool DIRECT>
 __global__ __launch_bounds__(64 * TOK) void k_disp_rank_gather(
-    const int32_t* __restrict__ ids, int64_t T, int k, int e_begin, int E_loc, int64_t nb, int parts, int tile_m,
+    const int32_t* __restrict__ ids, int64_t T, int k, int E_total, int e_begin, int E_loc, int64_t nb, int parts,
+    int tile_m,
     const int32_t* __restrict__ block_hist, const int32_t* __restrict__ block_err, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_offsets, int32_t* __restrict__ err,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, const u32x4_t* __restrict__ x, int row_chunks,
@@ -750,35 +752,52 @@ __global__ __launch_bounds__(64 * TOK) void k_disp_rank_gather(
   for (int i = tid; i < TOK * E_loc; i += kThreads) s_wcnt[i / E_loc][i % E_loc] = 0;
   __syncthreads();
   // 2. pairs before this workgroup's, and the totals
-  const int64_t cb = p_first / kMidPairsPerBlock;
-  if (tid < parts * E_loc) {
-    const int e = tid % E_loc;
-    const int part = tid / E_loc;
-    const int64_t per = (nb + parts - 1) / parts;
-    const int64_t r0 = min(nb, part * per);
-    const int64_t r1 = min(nb, r0 + per);
-    constexpr int U = 8;
-    int pre = 0, tot = 0;
-    for (int64_t r = r0; r < r1; r += U) {
-      int h[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) h[u] = r + u < r1 ? block_hist[(r + u) * E_loc + e] : 0;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        tot += h[u];
-        pre += r + u < cb ? h[u] : 0;
+  int any = 0;
+  if constexpr (DIRECT) {
+    // few pairs: every workgroup counts them all from the ids (no count
+    // kernel) and flags the ids outside [0, E)
+    for (int64_t q = tid; q < T * k; q += kThreads) {
+      const int id = ids[q];
+      if (id < 0 || id >= E_total) {
+        any = 1;
+        continue;
+      }
+      const int e = id - e_begin;
+      if (e >= 0 && e < E_loc) {
+        atomicAdd(&s_run[e], 1);
+        if (q < p_first) atomicAdd(&s_pre[e], 1);
       }
     }
-    if (pre) atomicAdd(&s_pre[e], pre);
-    if (tot) atomicAdd(&s_run[e], tot);
+  } else {
+    const int64_t cb = p_first / kMidPairsPerBlock;
+    if (tid < parts * E_loc) {
+      const int e = tid % E_loc;
+      const int part = tid / E_loc;
+      const int64_t per = (nb + parts - 1) / parts;
+      const int64_t r0 = min(nb, part * per);
+      const int64_t r1 = min(nb, r0 + per);
+      constexpr int U = 8;
+      int pre = 0, tot = 0;
+      for (int64_t r = r0; r < r1; r += U) {
+        int h[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) h[u] = r + u < r1 ? block_hist[(r + u) * E_loc + e] : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          tot += h[u];
+          pre += r + u < cb ? h[u] : 0;
+        }
+      }
+      if (pre) atomicAdd(&s_pre[e], pre);
+      if (tot) atomicAdd(&s_run[e], tot);
+    }
+    for (int64_t q = cb * kMidPairsPerBlock + tid; q < p_first; q += kThreads) {   // p_first <= T k
+      const int e = ids[q] - e_begin;
+      if (e >= 0 && e < E_loc) atomicAdd(&s_pre[e], 1);
+    }
+    if (g == 0)
+      for (int64_t q = tid; q < nb; q += kThreads) any |= block_err[q];
   }
-  for (int64_t q = cb * kMidPairsPerBlock + tid; q < p_first; q += kThreads) {   // p_first <= T k
-    const int e = ids[q] - e_begin;
-    if (e >= 0 && e < E_loc) atomicAdd(&s_pre[e], 1);
-  }
-  int any = 0;
-  if (g == 0)
-    for (int64_t q = tid; q < nb; q += kThreads) any |= block_err[q];
   any = __syncthreads_or(any);
   // 3. offsets
   const int cnt = tid < E_loc ? s_run[tid] : 0;
@@ -930,18 +949,23 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   // The mid-sized path with the rank folded into the gather (two launches);
   // beside an FFN launch the lean rank kernel and the gather run instead,
   // and a grid cap on the comm kernels keeps the three-launch form.
-  const bool fused = !a.beside_ffn && (n_pairs > kSmallMaxPairs || E_loc > kSmallMaxELoc) &&
-                     E_loc <= kMidMaxELoc && nb_mid * E_loc <= kFusedMaxHist && a.k <= kFusedMaxK &&
-                     (a.max_blocks <= 0 || groups <= a.max_blocks);
+  // Few pairs (decode): one kernel whose workgroups each count all the pairs
+  // from the ids themselves.
+  const bool small = n_pairs <= kSmallMaxPairs && E_loc <= kSmallMaxELoc;
+  const bool fused = !a.beside_ffn && a.T > 0 && E_loc <= kMidMaxELoc && a.k <= kFusedMaxK &&
+                     (small || nb_mid * E_loc <= kFusedMaxHist) && (a.max_blocks <= 0 || groups <= a.max_blocks);
   if (!fused) {
     const moe_status st = launch_dispatch_send(a, s);
     if (st != MOE_OK) return st;
     return launch_dispatch_recv(a, s);
   }
   DispWs w = carve(a.ws, n_pair_blocks(a.T, a.k), E_loc);
-  hipLaunchKernelGGL(k_disp_count<kMidPairsPerBlock>, dim3(static_cast<unsigned>(nb_mid)), dim3(kMidPairsPerBlock),
-                     0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist, w.block_err);
-  DBOMOE_CHECK_LAUNCH();
+  if (!small) {
+    hipLaunchKernelGGL(k_disp_count<kMidPairsPerBlock>, dim3(static_cast<unsigned>(nb_mid)),
+                       dim3(kMidPairsPerBlock), 0, s, a.ids, n_pairs, a.E_total, a.e_begin, E_loc, w.block_hist,
+                       w.block_err);
+    DBOMOE_CHECK_LAUNCH();
+  }
   const int parts = static_cast<int>(std::min<int64_t>(std::max(1, 64 * tok / E_loc), nb_mid));
   const int row_chunks = static_cast<int>(static_cast<int64_t>(a.H) * dtype_size(a.act) / 16);
   const int tile_m = a.tile_m > 0 ? a.tile_m : 1;
@@ -949,10 +973,16 @@ moe_status launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   auto launch_fused = [&](auto q8, auto tk) {
     constexpr bool Q8 = decltype(q8)::value;
     constexpr int TOK = decltype(tk)::value;
-    hipLaunchKernelGGL((k_disp_rank_gather<Q8, TOK>), dim3(static_cast<unsigned>(groups)), dim3(64 * TOK), 0, s,
-                       a.ids, a.T, a.k, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist, w.block_err,
-                       a.counts, a.offsets, tile_offsets, w.err, a.perm, a.inv, static_cast<const u32x4_t*>(a.x),
-                       row_chunks, a.x_perm, Q8 ? a.x_scale : nullptr);
+    if (small)
+      hipLaunchKernelGGL((k_disp_rank_gather<Q8, TOK, true>), dim3(static_cast<unsigned>(groups)), dim3(64 * TOK), 0,
+                         s, a.ids, a.T, a.k, a.E_total, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist,
+                         w.block_err, a.counts, a.offsets, tile_offsets, w.err, a.perm, a.inv,
+                         static_cast<const u32x4_t*>(a.x), row_chunks, a.x_perm, Q8 ? a.x_scale : nullptr);
+    else
+      hipLaunchKernelGGL((k_disp_rank_gather<Q8, TOK, false>), dim3(static_cast<unsigned>(groups)), dim3(64 * TOK), 0,
+                         s, a.ids, a.T, a.k, a.E_total, a.e_begin, E_loc, nb_mid, parts, tile_m, w.block_hist,
+                         w.block_err, a.counts, a.offsets, tile_offsets, w.err, a.perm, a.inv,
+                         static_cast<const u32x4_t*>(a.x), row_chunks, a.x_perm, Q8 ? a.x_scale : nullptr);
   };
   using T16 = std::integral_constant<int, 16>;
   using T4 = std::integral_constant<int, 4>;
